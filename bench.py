@@ -1,0 +1,182 @@
+"""Benchmark: batch-1 decode steps/s of the megakernel on a Llama-3.2-1B-shaped model.
+
+One "step" is one full decode step (every layer, attention over the cache, LM head and
+argmax) for one token, run as one kernel launch.  Default workload: Llama-3.2-1B shape,
+KV context 128, seeded synthetic bf16 weights, the step repeated at the same position
+(its K/V write is idempotent).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0).  Other workloads (--workload) are for the design notes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOADS = {
+    # name: (model shape, KV context / first position, greedy steps per timed step)
+    "llama1b_ctx128": ("llama1b", 128),
+    "llama1b_ctx8192": ("llama1b", 8192),
+    "llama1b_greedy_from_1024": ("llama1b", 1024),
+    "llama8b_ctx2048": ("llama8b", 2048),
+}
+METRIC = "batch-1 decode steps/sec (Llama-3.2-1B shape); achieved HBM GB/s vs peak"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_megakernel_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, n_launch_bytes: float):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, W, kv, tok, pos, budget_s=20.0):
+    """The CPU oracle (NumPy fp32, untuned) on this host, on a bounded sample of steps."""
+    import numpy as np
+
+    import oracle
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    Wn = W.as_numpy_bits()
+    kvn = kv.detach().cpu().view(__import__("torch").int16).numpy().view(np.uint16).copy()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_step(shape, Wn, kvn, tok, pos)
+        n += 1
+        el = time.perf_counter() - t0
+        if el > budget_s or n >= 8:
+            break
+    return dict(value=round(n / el, 4), unit="steps/s", cores=int(threads), kind="oracle",
+                sample=f"{n} decode steps of the same workload (NumPy fp32 oracle, {el:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama1b_ctx128", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "the decode megakernel has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_megakernel_amd import mk, roofline, synth
+
+    model, ctx = WORKLOADS[args.workload]
+    shape = synth.ModelShape.named(model)
+    dev = "cuda:0"
+    max_ctx = ctx + max(args.steps + args.warmup, 1) + 1
+    print(f"[bench] {args.workload}: generating weights", file=sys.stderr, flush=True)
+    W = synth.make_weights(shape, seed=0, device=dev)
+    kv = synth.make_kv_cache(shape, max_ctx, ctx, seed=1, device=dev)
+    tok = synth.make_token(shape, seed=2)
+    m = mk.Megakernel(shape, max_ctx, 0)
+    m.load_weights(W)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    tokbuf = torch.tensor([tok], dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    greedy = args.workload == "llama1b_greedy_from_1024"
+
+    def step(i):
+        if greedy:   # consecutive positions, token chained on the device
+            m.decode_step_dev(tokbuf, ctx + i, kv, logits, tokbuf, stream)
+        else:
+            m.decode_step(tok, ctx, kv, logits, nxt, stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i if not greedy else 0)
+    m.sync(stream)
+    if greedy:   # restart the chain so the timed steps walk positions ctx .. ctx+steps-1
+        tokbuf.fill_(tok)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    m.sync(stream)
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]) * 1e3   # us
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_per_step = total_ms / args.steps
+    pos_mid = ctx + (args.steps // 2 if greedy else 0)
+    bytes_step = roofline.step_bytes(shape, pos_mid)["total"]
+    avg_us = float(per.mean())
+    achieved = bytes_step / (avg_us * 1e-6) / 1e9
+    traffic = stored_traffic(args.workload, bytes_step)
+    out = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": {
+                "llama1b_ctx128": "Llama-3.2-1B-shaped batch-1 decode step, KV context 128",
+                "llama1b_ctx8192": "Llama-3.2-1B-shaped batch-1 decode step, KV context 8192",
+                "llama1b_greedy_from_1024": "Llama-3.2-1B-shaped greedy decode from context 1024, device-chained tokens",
+                "llama8b_ctx2048": "Llama-3.1-8B-shaped batch-1 decode step, KV context 2048",
+            }[args.workload],
+            "layers": shape.n_layers, "hidden": shape.hidden, "heads_q_kv": [shape.n_q_heads, shape.n_kv_heads],
+            "head_dim": shape.head_dim, "ffn": shape.ffn, "vocab": shape.vocab, "context": ctx,
+            "weights": "bf16", "activations_accumulate": "fp32",
+            "us_per_token": {"p50": round(float(np.percentile(per, 50)), 2),
+                             "p90": round(float(np.percentile(per, 90)), 2),
+                             "p99": round(float(np.percentile(per, 99)), 2),
+                             "min": round(float(per.min()), 2), "max": round(float(per.max()), 2)},
+            "algorithmic_bytes_per_step": bytes_step,
+            "wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": roofline.MI355X_HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / roofline.MI355X_HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(shape, W, kv, tok, ctx)
+    m.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

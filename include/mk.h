@@ -1,0 +1,161 @@
+/*
+ * mk.h — C ABI of the MI355X batch-1 decode megakernel library (libmk.so).
+ *
+ * One decode step of a Llama-style decoder runs as ONE persistent kernel launch, as
+ * in the Hazy Research "Megakernel" article on Llama-3.2-1B (section "Megakernel: a
+ * fusion design from scratch"): the whole forward pass — RMSNorm+QKV+RoPE, grouped-
+ * query attention over the cache, O-projection+residual, RMSNorm+SiLU(gate)*up,
+ * down-projection+residual, final RMSNorm+LM head — is executed by an on-GPU
+ * instruction interpreter following per-CU instruction lists that a host-side
+ * scheduler lays out once, before the first token, and reuses for every token.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (MK_OK) on success or a negative MK_E* code; no call throws.
+ *   - "device pointer" = memory on the context's HIP device (e.g. torch-allocated);
+ *     the library borrows it and never frees it.  The caller keeps it alive and
+ *     unmodified for as long as the context may use it.
+ *   - bf16 matrices are row-major [out][in] (a row is one output feature), dense.
+ *   - One context serves one stream at a time; calls on one context are not
+ *     thread-safe.  Work is asynchronous on the given stream unless stated.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_OK 0
+#define MK_EINVAL -1   /* null pointer, bad shape, unsupported configuration          */
+#define MK_ERANGE -2   /* pos >= max_ctx, or token outside [0, vocab)                  */
+#define MK_ESTATE -3   /* weights not loaded, or context in an unusable state         */
+#define MK_EHIP -4     /* a HIP runtime call failed; mk_strerror() names it            */
+#define MK_ETIMEOUT -5 /* a device-side bounded wait expired (the step was abandoned) */
+#define MK_ENOMEM -6   /* device allocation failed                                    */
+
+/* Model shape and numerics.  The article's model is Llama-3.2-1B: 16 layers, hidden
+ * 2048, 32 query / 8 KV heads of 64, SwiGLU 8192, vocab 128256.  Supported here:
+ * head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with at most 8 query
+ * heads per KV head; hidden, ffn and n_q_heads*head_dim multiples of 256 and at most
+ * 4096*? (see mk_create); ffn/4 a multiple of 64 bf16 (the down projection is
+ * consumed in 4 chunks, after the article's 4-chunk MLP intermediate). */
+typedef struct mk_config {
+  int32_t n_layers;
+  int32_t hidden;      /* d                                   */
+  int32_t n_q_heads;   /* Hq                                  */
+  int32_t n_kv_heads;  /* Hkv                                 */
+  int32_t head_dim;    /* hd                                  */
+  int32_t ffn;         /* F (SwiGLU intermediate)             */
+  int32_t vocab;       /* V                                   */
+  int32_t max_ctx;     /* KV-cache slots per (layer, kv head) */
+  float rms_eps;       /* RMSNorm epsilon, inside the root    */
+  float rope_theta;    /* RoPE base (rotate-half pairing)     */
+} mk_config;
+
+/* Borrowed device pointers to bf16 weights.  The per-layer entries are HOST arrays of
+ * n_layers device pointers each; the library copies the arrays, not the weights.
+ *   embed      [vocab][hidden]      token embedding (row gathered, not scaled)
+ *   lm_head    [vocab][hidden]      may equal embed (tied)
+ *   final_norm [hidden]             RMSNorm gain before the LM head
+ *   attn_norm  [hidden]             per layer, gain before QKV
+ *   wq [Hq*hd][hidden], wk [Hkv*hd][hidden], wv [Hkv*hd][hidden]
+ *   wo [hidden][Hq*hd]
+ *   mlp_norm   [hidden]             per layer, gain before gate/up
+ *   w_gate, w_up [ffn][hidden], w_down [hidden][ffn]                              */
+typedef struct mk_weights {
+  const void* embed;
+  const void* lm_head;
+  const void* final_norm;
+  const void* const* attn_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* mlp_norm;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+} mk_weights;
+
+typedef struct mk_ctx mk_ctx;
+
+/* Create a context for `cfg` on HIP device `hip_device`.  Validates the shape,
+ * queries the device (compute units, LDS) and allocates nothing yet.
+ * Errors: MK_EINVAL (null/unsupported shape), MK_EHIP (no such device). */
+int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out);
+
+/* Record the weight pointers and build the static schedule: per-CU instruction lists
+ * (article: plans laid out statically before runtime and reused for every token),
+ * the device-side communication buffers, the RoPE cos/sin table [max_ctx][hd/2]
+ * (fp32, computed in double on the host) and the control block.  Synchronous;
+ * allocates with hipMalloc.  May be called again to switch weights.
+ * Errors: MK_EINVAL, MK_ENOMEM, MK_EHIP. */
+int mk_load_weights(mk_ctx* ctx, const mk_weights* w);
+
+/* One decode step (asynchronous on `stream`, a hipStream_t; NULL = default stream).
+ *   token      input token id, in [0, vocab)
+ *   pos        its position; keys 0..pos are attended; 0 <= pos < max_ctx
+ *   kv_cache   device bf16 [n_layers][2 (K,V)][n_kv_heads][max_ctx][head_dim];
+ *              slots [0, pos) must hold the keys (already rotated) and values of the
+ *              prefix; slot pos of every layer is overwritten with the new K, V
+ *              (rounded to bf16, round-to-nearest-even); other slots are not written.
+ *   logits_out device fp32 [vocab]: logits of the next token.
+ *   next_token device int32 [1] or NULL: receives argmax(logits), lowest index on ties.
+ * Errors: MK_ESTATE (no weights), MK_ERANGE, MK_EINVAL (null kv/logits), MK_EHIP.
+ * A device-side watchdog failure is reported by the next mk_sync(). */
+int mk_decode_step(mk_ctx* ctx, int32_t token, int32_t pos, void* kv_cache,
+                   float* logits_out, int32_t* next_token, void* stream);
+
+/* As mk_decode_step, but the token is read on the device from token_dev (device
+ * int32 [1]) when the step starts — e.g. the previous step's next_token — so a
+ * greedy loop needs no host synchronisation between steps.  token_dev and
+ * next_token may be the same buffer.  Out-of-range device tokens are clamped to
+ * [0, vocab) by the kernel and flagged as MK_ERANGE at the next mk_sync(). */
+int mk_decode_step_dev(mk_ctx* ctx, const int32_t* token_dev, int32_t pos, void* kv_cache,
+                       float* logits_out, int32_t* next_token, void* stream);
+
+/* Wait for the context's outstanding steps on `stream` and surface device-side
+ * errors (MK_ETIMEOUT, MK_ERANGE for a clamped device token).  After an error the
+ * context resets its device state on the next step. */
+int mk_sync(mk_ctx* ctx, void* stream);
+
+/* Device-side wait budget in microseconds (default 2,000,000).  Every bounded wait in
+ * the kernel gives up after this long, records MK_ETIMEOUT and exits. */
+int mk_set_watchdog_us(mk_ctx* ctx, int64_t us);
+
+/* Schedule introspection (host only; valid after mk_load_weights or mk_plan_only).
+ * mk_plan_info fills: [0] number of CUs planned, [1] instruction record size in
+ * int32 words, [2] total records, [3] page bytes, [4] pages per compute wave,
+ * [5] compute waves per CU, [6] attention splits per KV head, [7] LDS bytes.
+ * mk_plan_copy copies `n_cus`+1 list offsets then the records (int32 words). */
+int mk_plan_info(const mk_ctx* ctx, int32_t info[8]);
+int mk_plan_copy(const mk_ctx* ctx, int32_t* offsets, int32_t* records, int64_t records_capacity_words);
+
+/* Build only the static schedule for a hypothetical device with `n_cus` compute units
+ * (no HIP calls, no allocation on any device): for host-side tests of the scheduler. */
+int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out);
+
+/* Debug: copy the device communication words of the last step to host memory
+ * (synchronous).  Each word is (fp32 value | epoch << 32).  offsets[0..5] receive the
+ * word offsets of: x after each residual [2L+1][hidden] (entry 0 unused), raw q/k/v
+ * [L][kv head][q heads of the group | k | v][head_dim], split partials, attention
+ * output [L][Hq*hd], SiLU(gate)*up [L][ffn], and the total word count; `host` may be
+ * NULL to query the offsets only.  Errors: MK_ESTATE before mk_load_weights. */
+int mk_debug_dump(const mk_ctx* ctx, uint64_t* host, int64_t capacity_words, int64_t offsets[6]);
+
+/* Free everything the context allocated (not the borrowed weights or caches). */
+void mk_destroy(mk_ctx* ctx);
+
+/* Static text for an MK_* code (for MK_EHIP, the last HIP error of this thread). */
+const char* mk_strerror(int code);
+
+/* Library version string. */
+const char* mk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -113,14 +113,16 @@ def gemv(W_bits: np.ndarray, x: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- the decode step
 def decode_step(cfg, W: dict, kv: np.ndarray, token: int, pos: int, dtype=np.float32,
-                return_next: bool = False):
+                return_next: bool = False, trace: dict = None):
     """One decode step: process ``token`` at position ``pos``.
 
     ``cfg`` has attributes n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn,
     vocab, rms_eps, rope_theta.  ``W`` maps names to uint16 bf16-bit arrays (lists
     per layer).  ``kv`` is the uint16 cache [layer][k|v][kv_head][max_ctx][hd]; slot
     ``pos`` of every layer is overwritten (in place) with the new rounded K and V.
-    Returns the logits (``dtype``, length vocab), and the argmax when asked.
+    Returns the logits (``dtype``, length vocab), and the argmax when asked.  When
+    ``trace`` is a dict it receives the intermediates per layer: raw q/k/v (before
+    RoPE), attention output o, SiLU(gate)*up, and x after each residual add.
     """
     hd, Hq, Hkv = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
     eps = cfg.rms_eps
@@ -135,6 +137,10 @@ def decode_step(cfg, W: dict, kv: np.ndarray, token: int, pos: int, dtype=np.flo
         q = gemv(W["wq"][layer], n).reshape(Hq, hd)
         k = gemv(W["wk"][layer], n).reshape(Hkv, hd)
         v = gemv(W["wv"][layer], n).reshape(Hkv, hd)
+        if trace is not None:
+            trace.setdefault("q", []).append(q.copy())
+            trace.setdefault("k", []).append(k.copy())
+            trace.setdefault("v", []).append(v.copy())
         q = apply_rope(q, cos, sin)
         k = apply_rope(k, cos, sin)
         kv[layer, 0, :, pos, :] = float_to_bf16(k)
@@ -148,11 +154,17 @@ def decode_step(cfg, W: dict, kv: np.ndarray, token: int, pos: int, dtype=np.flo
             o[h] = attend_one_head(q[h], K, V)
         # 3. O-projection + residual
         x = x + gemv(W["wo"][layer], o.reshape(-1))
+        if trace is not None:
+            trace.setdefault("o", []).append(o.reshape(-1).copy())
+            trace.setdefault("x", []).append(x.copy())
         # 4. MLP RMSNorm + SiLU(gate) * up
         n2 = rms_norm(x, bf16_to_float(W["mlp_norm"][layer], dtype), eps)
         a = silu(gemv(W["w_gate"][layer], n2)) * gemv(W["w_up"][layer], n2)
         # 5. down projection + residual
         x = x + gemv(W["w_down"][layer], a)
+        if trace is not None:
+            trace.setdefault("a", []).append(a.copy())
+            trace["x"].append(x.copy())
     # 6. final RMSNorm + LM head
     nf = rms_norm(x, bf16_to_float(W["final_norm"], dtype), eps)
     logits = gemv(W["lm_head"], nf)

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI and the static scheduler (no GPU needed)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from transformer_megakernel_amd import mk
+from transformer_megakernel_amd.synth import ModelShape
+
+OPS = dict(QKV=1, ATTN=2, O=3, GATEUP=4, DOWN=5, LMHEAD=6)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mk.lib()
+    names = mk.header_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.mk_version()
+
+
+def test_error_codes_without_a_usable_device():
+    cfg = mk.make_config(ModelShape.named("tiny"), 64)
+    h = ctypes.c_void_p()
+    assert mk.lib().mk_create(None, 0, ctypes.byref(h)) == mk.MK_EINVAL
+    bad = mk.make_config(ModelShape.named("tiny"), 64)
+    bad.head_dim = 96
+    assert mk.lib().mk_create(ctypes.byref(bad), 0, ctypes.byref(h)) == mk.MK_EINVAL
+    assert b"head_dim" in mk.lib().mk_strerror(mk.MK_EINVAL)
+    # a bad device index is rejected, whether or not a GPU is present
+    rc = mk.lib().mk_create(ctypes.byref(cfg), 4096, ctypes.byref(h))
+    assert rc in (mk.MK_EINVAL, mk.MK_EHIP)
+    assert mk.lib().mk_decode_step(None, 0, 0, None, None, None, None) == mk.MK_EINVAL
+    assert mk.lib().mk_sync(None, None) == mk.MK_EINVAL
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(mk.lib().mk_strerror(code), bytes)
+
+
+@pytest.mark.parametrize("field,value", [("n_q_heads", 3), ("n_kv_heads", 3), ("hidden", 96),
+                                         ("ffn", 100), ("hidden", 8192), ("max_ctx", 0)])
+def test_config_validation_rejects_unsupported_shapes(field, value):
+    cfg = mk.make_config(ModelShape.named("tiny"), 64)
+    setattr(cfg, field, value)
+    h = ctypes.c_void_p()
+    assert mk.lib().mk_plan_only(ctypes.byref(cfg), 256, ctypes.byref(h)) == mk.MK_EINVAL
+
+
+def _split(n, parts, i):
+    return n * i // parts, n * (i + 1) // parts
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b", "llama8b"])
+@pytest.mark.parametrize("n_cus", [256, 240, 80])
+def test_plan_partitions_every_matrix_exactly(name, n_cus):
+    s = ModelShape.named(name)
+    try:
+        m = mk.Megakernel.plan_only(s, 4096, n_cus)
+    except mk.MkError:
+        assert n_cus == 80 and name == "llama8b"   # 4096 / 80 > 64 residual rows per CU
+        return
+    P = m.plan()
+    off, rec = P["offsets"], P["records"]
+    nq, nkv = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    nqkv = nq + 2 * nkv
+    cover = {}
+    for cu in range(n_cus):
+        lst = rec[off[cu]:off[cu + 1]]
+        assert lst[-1, 0] == OPS["LMHEAD"]
+        phase = [(r[1], r[0]) for r in lst]
+        assert phase == sorted(phase), "list not in phase order"
+        o_rows = None
+        for r in lst:
+            op, layer, r0, n, k0, kn, a, b, rr0, rn = r[:10]
+            cover.setdefault((op, layer, a if op == OPS["DOWN"] else 0), []).append((r0, n, k0, kn, a, b))
+            if op == OPS["QKV"]:
+                o_rows = (rr0, rn)
+                assert (k0, kn) == (0, s.hidden)
+            if op == OPS["O"]:
+                assert (r0, n) == o_rows and (k0, kn) == (0, nq)
+            if op == OPS["GATEUP"]:
+                assert (rr0, rn) == o_rows
+            if op == OPS["DOWN"]:
+                assert (r0, n) == o_rows and kn == s.ffn // b and k0 == a * kn
+    for l in range(s.n_layers):
+        for op, total in ((OPS["QKV"], nqkv), (OPS["O"], s.hidden), (OPS["GATEUP"], s.ffn)):
+            rows = sorted((r0, n) for r0, n, *_ in cover[(op, l, 0)] if n > 0)
+            pos = 0
+            for r0, n in rows:
+                assert r0 == pos
+                pos += n
+            assert pos == total
+        nch = cover[(OPS["DOWN"], l, 0)][0][5]
+        for k in range(nch):
+            rows = sorted((r0, n) for r0, n, *_ in cover[(OPS["DOWN"], l, k)])
+            assert sum(n for _, n in rows) == s.hidden
+        items = sorted((a, b) for *_, a, b in cover[(OPS["ATTN"], l, 0)])
+        assert items == [(g, t) for g in range(s.n_kv_heads) for t in range(P["s_max"])]
+    lm = sorted((r0, n) for r0, n, *_ in cover[(OPS["LMHEAD"], s.n_layers, 0)])
+    assert sum(n for _, n in lm) == s.vocab and len(lm) == n_cus
+    assert P["lds_bytes"] <= 160 * 1024
+    assert P["page_bytes"] * P["pages_per_wave"] * P["compute_waves"] <= 128 * 1024
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b", "llama8b"])
+@pytest.mark.parametrize("pos", [0, 16, 128, 300, 1279, 8192])
+def test_plan_has_no_deadlock_at_any_position(name, pos):
+    """Discrete-event run of the per-CU lists with the device's dependency rules: every
+    CU executes its list in order, an instruction runs once everything it reads exists."""
+    from tests.plan_sim import simulate
+    s = ModelShape.named(name)
+    m = mk.Megakernel.plan_only(s, 8193, 256)
+    done, steps = simulate(s, m.plan(), pos)
+    assert done, f"deadlock after {steps} rounds"

@@ -1,0 +1,387 @@
+// C ABI of the decode megakernel library: context, static schedule upload, launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_kernel.h"
+#include "mk_plan.h"
+
+struct mk_ctx {
+  mk_config cfg{};
+  int device = -1;
+  int n_cus = 0;
+  bool plan_only = false;
+  bool loaded = false;
+  bool needs_reset = false;
+  long long watchdog_us = 2000000;
+  MkPlan plan;
+  // borrowed weights
+  const uint16_t* embed = nullptr;
+  const uint16_t* lm_head = nullptr;
+  const uint16_t* final_norm = nullptr;
+  // owned device memory
+  MkLayerPtrs* d_layers = nullptr;
+  int32_t* d_off = nullptr;
+  MkInstr* d_plan = nullptr;
+  float* d_rope = nullptr;
+  unsigned long long* d_ll = nullptr;
+  size_t ll_words = 0;
+  size_t off_x = 0, off_qkv = 0, off_part = 0, off_o = 0, off_a = 0;
+  unsigned long long* d_amax = nullptr;
+  MkCtrl* d_ctrl = nullptr;
+  int32_t* d_next = nullptr;   // argmax sink when the caller passes none
+};
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s", what, hipGetErrorString(e));
+  return MK_EHIP;
+}
+
+#define HIPCHK(call)                                  \
+  do {                                                \
+    hipError_t e_ = (call);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+void free_device(mk_ctx* c) {
+  if (c->plan_only) return;
+  void* ptrs[] = {c->d_layers, c->d_off, c->d_plan, c->d_rope, c->d_ll, c->d_amax, c->d_ctrl, c->d_next};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  c->d_layers = nullptr;
+  c->d_off = nullptr;
+  c->d_plan = nullptr;
+  c->d_rope = nullptr;
+  c->d_ll = nullptr;
+  c->d_amax = nullptr;
+  c->d_ctrl = nullptr;
+  c->d_next = nullptr;
+  c->loaded = false;
+}
+
+int reset_device_state(mk_ctx* c, hipStream_t s) {
+  HIPCHK(hipMemsetAsync(c->d_ll, 0, c->ll_words * sizeof(unsigned long long), s));
+  MkCtrl ctrl{};
+  ctrl.epoch = 1;
+  HIPCHK(hipMemcpyAsync(c->d_ctrl, &ctrl, sizeof(ctrl), hipMemcpyHostToDevice, s));
+  HIPCHK(hipStreamSynchronize(s));
+  c->needs_reset = false;
+  return MK_OK;
+}
+
+int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void* kv, float* logits,
+           int32_t* next_token, hipStream_t s) {
+  if (!c) return MK_EINVAL;
+  if (!c->loaded || c->plan_only) return MK_ESTATE;
+  if (!kv || !logits) return MK_EINVAL;
+  if (pos < 0 || pos >= c->cfg.max_ctx) return MK_ERANGE;
+  if (!token_dev && (token < 0 || token >= c->cfg.vocab)) return MK_ERANGE;
+  HIPCHK(hipSetDevice(c->device));
+  if (c->needs_reset) {
+    int rc = reset_device_state(c, s);
+    if (rc) return rc;
+  }
+  const mk_config& g = c->cfg;
+  MkParams p{};
+  p.n_layers = g.n_layers;
+  p.d = g.hidden;
+  p.hq = g.n_q_heads;
+  p.hkv = g.n_kv_heads;
+  p.hd = g.head_dim;
+  p.F = g.ffn;
+  p.V = g.vocab;
+  p.max_ctx = g.max_ctx;
+  p.nq = g.n_q_heads * g.head_dim;
+  p.nkv = g.n_kv_heads * g.head_dim;
+  p.nqkv = p.nq + 2 * p.nkv;
+  p.hpg = g.n_q_heads / g.n_kv_heads;
+  p.eps = g.rms_eps;
+  p.attn_scale = (float)(1.0 / std::sqrt((double)g.head_dim));
+  p.n_cus = c->plan.n_cus;
+  p.page_bytes = c->plan.page_bytes;
+  p.npw = c->plan.npw;
+  p.lpp = c->plan.page_bytes / 1024;
+  p.s_max = c->plan.s_max;
+  p.min_chunk = c->plan.min_chunk;
+  p.embed = c->embed;
+  p.lm_head = c->lm_head;
+  p.final_norm = c->final_norm;
+  p.layers = c->d_layers;
+  p.rope = c->d_rope;
+  p.plan_off = c->d_off;
+  p.plan = c->d_plan;
+  p.ll_x = c->d_ll + c->off_x;
+  p.ll_qkv = c->d_ll + c->off_qkv;
+  p.ll_part = c->d_ll + c->off_part;
+  p.ll_o = c->d_ll + c->off_o;
+  p.ll_a = c->d_ll + c->off_a;
+  p.amax = c->d_amax;
+  p.ctrl = c->d_ctrl;
+  p.kv = (uint16_t*)kv;
+  p.logits = logits;
+  p.next_token = next_token ? next_token : c->d_next;
+  p.token_dev = token_dev;
+  p.token = token;
+  p.pos = pos;
+  p.watchdog_ticks = c->watchdog_us * 100;   // s_memrealtime runs at 100 MHz
+  void* args[] = {&p};
+  HIPCHK(hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(c->plan.n_cus), dim3(MK_THREADS), args, 0,
+                                    s));
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
+  if (!cfg || !out) return MK_EINVAL;
+  *out = nullptr;
+  std::string why;
+  if (mk_check_config(*cfg, &why)) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", why.c_str());
+    return MK_EINVAL;
+  }
+  int n = 0;
+  HIPCHK(hipGetDeviceCount(&n));
+  if (hip_device < 0 || hip_device >= n) return MK_EINVAL;
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, hip_device));
+  int coop = 0;
+  HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, hip_device));
+  if (!coop) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "device %d lacks cooperative launch", hip_device);
+    return MK_EHIP;
+  }
+  mk_ctx* c = new mk_ctx();
+  c->cfg = *cfg;
+  c->device = hip_device;
+  c->n_cus = prop.multiProcessorCount;
+  *out = c;
+  return MK_OK;
+}
+
+int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out) {
+  if (!cfg || !out) return MK_EINVAL;
+  *out = nullptr;
+  mk_ctx* c = new mk_ctx();
+  c->cfg = *cfg;
+  c->plan_only = true;
+  c->n_cus = n_cus;
+  std::string why;
+  int rc = mk_build_plan(*cfg, n_cus, &c->plan, &why);
+  if (rc) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", why.c_str());
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return MK_OK;
+}
+
+int mk_load_weights(mk_ctx* c, const mk_weights* w) {
+  if (!c || !w) return MK_EINVAL;
+  if (c->plan_only) return MK_ESTATE;
+  const mk_config& g = c->cfg;
+  if (!w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return MK_EINVAL;
+  // n_layers + 1 entries: the extra one carries the final norm gain for the LM head.
+  std::vector<MkLayerPtrs> layers(g.n_layers + 1);
+  for (int l = 0; l < g.n_layers; ++l) {
+    MkLayerPtrs& L = layers[l];
+    L.attn_norm = (const uint16_t*)w->attn_norm[l];
+    L.wq = (const uint16_t*)w->wq[l];
+    L.wk = (const uint16_t*)w->wk[l];
+    L.wv = (const uint16_t*)w->wv[l];
+    L.wo = (const uint16_t*)w->wo[l];
+    L.mlp_norm = (const uint16_t*)w->mlp_norm[l];
+    L.wg = (const uint16_t*)w->w_gate[l];
+    L.wu = (const uint16_t*)w->w_up[l];
+    L.wd = (const uint16_t*)w->w_down[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.mlp_norm || !L.wg || !L.wu || !L.wd)
+      return MK_EINVAL;
+    // 16-byte alignment: rows are streamed with 16-byte loads
+    const void* ps[] = {L.wq, L.wk, L.wv, L.wo, L.wg, L.wu, L.wd};
+    for (const void* q : ps)
+      if ((uintptr_t)q & 15) return MK_EINVAL;
+    if (((uintptr_t)L.attn_norm & 3) || ((uintptr_t)L.mlp_norm & 3)) return MK_EINVAL;
+  }
+  if (((uintptr_t)w->lm_head & 15) || ((uintptr_t)w->final_norm & 3)) return MK_EINVAL;
+  layers[g.n_layers] = MkLayerPtrs{};
+  layers[g.n_layers].attn_norm = (const uint16_t*)w->final_norm;
+  std::string why;
+  MkPlan plan;
+  int rc = mk_build_plan(g, c->n_cus, &plan, &why);
+  if (rc) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", why.c_str());
+    return rc;
+  }
+  HIPCHK(hipSetDevice(c->device));
+  free_device(c);
+  c->plan = std::move(plan);
+  c->embed = (const uint16_t*)w->embed;
+  c->lm_head = (const uint16_t*)w->lm_head;
+  c->final_norm = (const uint16_t*)w->final_norm;
+
+  // RoPE table [max_ctx][hd/2][cos, sin], angles in double, rounded to fp32.
+  const int half = g.head_dim / 2;
+  std::vector<float> rope((size_t)g.max_ctx * half * 2);
+  for (int pos = 0; pos < g.max_ctx; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)g.rope_theta, -2.0 * i / g.head_dim);
+      const double ang = (double)pos * inv;
+      rope[((size_t)pos * half + i) * 2] = (float)std::cos(ang);
+      rope[((size_t)pos * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+
+  const int hpg = g.n_q_heads / g.n_kv_heads;
+  const size_t nq = (size_t)g.n_q_heads * g.head_dim, nqkv = nq + 2 * (size_t)g.n_kv_heads * g.head_dim;
+  c->off_x = 0;
+  c->off_qkv = c->off_x + (size_t)(2 * g.n_layers + 1) * g.hidden;
+  c->off_part = c->off_qkv + (size_t)g.n_layers * nqkv;
+  c->off_o = c->off_part + (size_t)g.n_layers * g.n_kv_heads * hpg * c->plan.s_max * (g.head_dim + 2);
+  c->off_a = c->off_o + (size_t)g.n_layers * nq;
+  c->ll_words = c->off_a + (size_t)g.n_layers * g.ffn;
+
+  auto alloc = [&](void** p, size_t bytes) -> int {
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+      hip_fail(e, "hipMalloc");
+      return MK_ENOMEM;
+    }
+    return MK_OK;
+  };
+  if ((rc = alloc((void**)&c->d_layers, layers.size() * sizeof(MkLayerPtrs))) ||
+      (rc = alloc((void**)&c->d_off, c->plan.off.size() * sizeof(int32_t))) ||
+      (rc = alloc((void**)&c->d_plan, c->plan.rec.size() * sizeof(MkInstr))) ||
+      (rc = alloc((void**)&c->d_rope, rope.size() * sizeof(float))) ||
+      (rc = alloc((void**)&c->d_ll, c->ll_words * sizeof(unsigned long long))) ||
+      (rc = alloc((void**)&c->d_amax, c->plan.n_cus * sizeof(unsigned long long))) ||
+      (rc = alloc((void**)&c->d_ctrl, sizeof(MkCtrl))) || (rc = alloc((void**)&c->d_next, 64))) {
+    free_device(c);
+    return rc;
+  }
+  HIPCHK(hipMemcpy(c->d_layers, layers.data(), layers.size() * sizeof(MkLayerPtrs), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(c->d_off, c->plan.off.data(), c->plan.off.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(c->d_plan, c->plan.rec.data(), c->plan.rec.size() * sizeof(MkInstr), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(c->d_rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice));
+  HIPCHK(hipMemset(c->d_amax, 0, c->plan.n_cus * sizeof(unsigned long long)));
+  HIPCHK(hipMemset(c->d_next, 0, 64));
+  c->loaded = true;
+  rc = reset_device_state(c, nullptr);
+  if (rc) return rc;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_ctx* c, int32_t token, int32_t pos, void* kv_cache, float* logits_out,
+                   int32_t* next_token, void* stream) {
+  return launch(c, token, nullptr, pos, kv_cache, logits_out, next_token, (hipStream_t)stream);
+}
+
+int mk_decode_step_dev(mk_ctx* c, const int32_t* token_dev, int32_t pos, void* kv_cache, float* logits_out,
+                       int32_t* next_token, void* stream) {
+  if (!token_dev) return MK_EINVAL;
+  return launch(c, 0, token_dev, pos, kv_cache, logits_out, next_token, (hipStream_t)stream);
+}
+
+int mk_sync(mk_ctx* c, void* stream) {
+  if (!c) return MK_EINVAL;
+  if (!c->loaded) return MK_ESTATE;
+  HIPCHK(hipSetDevice(c->device));
+  HIPCHK(hipStreamSynchronize((hipStream_t)stream));
+  MkCtrl ctrl{};
+  HIPCHK(hipMemcpy(&ctrl, c->d_ctrl, sizeof(ctrl), hipMemcpyDeviceToHost));
+  if (ctrl.error != 0) {
+    c->needs_reset = true;
+    return ctrl.error;
+  }
+  if (ctrl.bad_token) {
+    c->needs_reset = true;
+    return MK_ERANGE;
+  }
+  return MK_OK;
+}
+
+int mk_set_watchdog_us(mk_ctx* c, int64_t us) {
+  if (!c || us < 0) return MK_EINVAL;
+  c->watchdog_us = us;
+  return MK_OK;
+}
+
+int mk_plan_info(const mk_ctx* c, int32_t info[8]) {
+  if (!c || !info) return MK_EINVAL;
+  if (c->plan.off.empty()) return MK_ESTATE;
+  info[0] = c->plan.n_cus;
+  info[1] = MK_INSTR_WORDS;
+  info[2] = (int32_t)c->plan.rec.size();
+  info[3] = c->plan.page_bytes;
+  info[4] = c->plan.npw;
+  info[5] = MK_NC;
+  info[6] = c->plan.s_max;
+  info[7] = (int32_t)sizeof(mkdev::MkShared);
+  return MK_OK;
+}
+
+int mk_plan_copy(const mk_ctx* c, int32_t* offsets, int32_t* records, int64_t cap_words) {
+  if (!c || !offsets || !records) return MK_EINVAL;
+  if (c->plan.off.empty()) return MK_ESTATE;
+  if (cap_words < (int64_t)c->plan.rec.size() * MK_INSTR_WORDS) return MK_EINVAL;
+  memcpy(offsets, c->plan.off.data(), c->plan.off.size() * sizeof(int32_t));
+  memcpy(records, c->plan.rec.data(), c->plan.rec.size() * sizeof(MkInstr));
+  return MK_OK;
+}
+
+int mk_debug_dump(const mk_ctx* c, uint64_t* host, int64_t cap, int64_t offsets[6]) {
+  if (!c || !offsets) return MK_EINVAL;
+  if (!c->loaded) return MK_ESTATE;
+  offsets[0] = (int64_t)c->off_x;
+  offsets[1] = (int64_t)c->off_qkv;
+  offsets[2] = (int64_t)c->off_part;
+  offsets[3] = (int64_t)c->off_o;
+  offsets[4] = (int64_t)c->off_a;
+  offsets[5] = (int64_t)c->ll_words;
+  if (!host) return MK_OK;
+  if (cap < (int64_t)c->ll_words) return MK_EINVAL;
+  HIPCHK(hipSetDevice(c->device));
+  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemcpy(host, c->d_ll, c->ll_words * sizeof(uint64_t), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+void mk_destroy(mk_ctx* c) {
+  if (!c) return;
+  if (!c->plan_only && c->device >= 0) {
+    (void)hipSetDevice(c->device);
+    free_device(c);
+  }
+  delete c;
+}
+
+const char* mk_strerror(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_EINVAL: return g_hip_msg[0] ? g_hip_msg : "invalid argument";
+    case MK_ERANGE: return "position or token out of range";
+    case MK_ESTATE: return "weights not loaded / wrong state";
+    case MK_EHIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+    case MK_ETIMEOUT: return "device-side wait expired (step abandoned)";
+    case MK_ENOMEM: return "device allocation failed";
+    default: return "unknown error";
+  }
+}
+
+const char* mk_version(void) { return "mk 0.1.0 (gfx950)"; }
+
+}  // extern "C"
+
+#include "mk_plan.cpp"

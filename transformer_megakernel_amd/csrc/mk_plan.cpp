@@ -1,0 +1,153 @@
+// Host-side static scheduler.
+//
+// The Megakernel article (section "Megakernel: a fusion design from scratch") lays
+// out every SM's instruction list before runtime, by model structure, with no
+// dynamic branching in scheduling, and reuses it for every token.  Here the lists
+// are per CU of a gfx950 part: every matrix of the step is cut into contiguous row
+// ranges, one per CU, so that each CU streams an equal share of every phase's bytes
+// (a phase is one instruction of one layer).  Attention is cut into (KV head, split)
+// items whose key ranges are derived from the position on the device, so the same
+// plan serves every context length.
+//
+// Every list is ordered by phase (layer-major, then the article's instruction
+// order), and an instruction only consumes results of strictly earlier phases, so
+// with all work-groups resident no CU can wait on work queued behind itself.
+#include "mk_plan.h"
+
+#include <algorithm>
+
+namespace {
+
+bool seg_ok(int k_elems) {
+  long bytes = 2L * k_elems;
+  if (bytes <= 0) return false;
+  if (bytes < 1024) return bytes >= 256 && (bytes & (bytes - 1)) == 0;   // <= 64 rows per page
+  return bytes % 1024 == 0;
+}
+
+int down_chunks(const mk_config& c) {
+  // The article splits the MLP intermediate into 4 chunks so the down projection
+  // can start on a chunk as soon as it is written.
+  for (int nch : {4, 2, 1})
+    if (c.ffn % nch == 0 && seg_ok(c.ffn / nch) && c.ffn / nch <= MK_ACT_FLOATS) return nch;
+  return 0;
+}
+
+int pick_page_bytes(const mk_config& c, int nch) {
+  long need = std::max<long>({4L * c.hidden,                   // a gate row and its up row
+                              2L * c.n_q_heads * c.head_dim,   // one O row
+                              2L * (c.ffn / std::max(nch, 1)), // one DOWN chunk row
+                              4L * c.head_dim});               // one key and its value
+  for (int pb : {8192, 16384})
+    if (need <= pb) return pb;
+  return 0;
+}
+
+void split(int n, int parts, int i, int* r0, int* cnt) {
+  long a = (long)n * i / parts, b = (long)n * (i + 1) / parts;
+  *r0 = (int)a;
+  *cnt = (int)(b - a);
+}
+
+MkInstr mk(int op, int layer) {
+  MkInstr x{};
+  x.op = op;
+  x.layer = layer;
+  return x;
+}
+
+}  // namespace
+
+int mk_check_config(const mk_config& c, std::string* why) {
+  auto bad = [&](const char* m) {
+    if (why) *why = m;
+    return MK_EINVAL;
+  };
+  if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.ffn < 1 ||
+      c.vocab < 1 || c.max_ctx < 1)
+    return bad("every dimension must be positive");
+  if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (c.n_q_heads % c.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+  int hpg = c.n_q_heads / c.n_kv_heads;
+  if (hpg != 1 && hpg != 2 && hpg != 4) return bad("query heads per KV head must be 1, 2 or 4");
+  if ((hpg + 2) * c.head_dim > MK_PART_OFF) return bad("(q heads per group + 2) * head_dim exceeds 1024");
+  if (MK_NC * hpg * (c.head_dim + 2) > MK_ACT_FLOATS - MK_PART_OFF) return bad("attention partials exceed LDS");
+  if (c.hidden > MK_ACT_FLOATS || c.n_q_heads * c.head_dim > MK_ACT_FLOATS)
+    return bad("hidden and n_q_heads*head_dim must be <= 4096");
+  if (!seg_ok(c.hidden) || !seg_ok(c.n_q_heads * c.head_dim))
+    return bad("hidden and n_q_heads*head_dim must be 128, 256 or a multiple of 512");
+  int nch = down_chunks(c);
+  if (!nch) return bad("ffn/4 (or ffn/2, ffn) must be 128, 256 or a multiple of 512, and <= 4096");
+  if (!pick_page_bytes(c, nch)) return bad("rows too long for a 16 KiB page");
+  if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0f)) return bad("rms_eps must be >= 0 and rope_theta > 0");
+  return MK_OK;
+}
+
+int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) {
+  int rc = mk_check_config(c, why);
+  if (rc) return rc;
+  if (n_cus < 1) {
+    if (why) *why = "n_cus must be positive";
+    return MK_EINVAL;
+  }
+  if ((c.hidden + n_cus - 1) / n_cus > MK_MAX_RES_ROWS) {
+    if (why) *why = "hidden / n_cus exceeds the 64 residual rows one CU may own";
+    return MK_EINVAL;
+  }
+  const int nch = down_chunks(c);
+  MkPlan p;
+  p.n_cus = n_cus;
+  p.page_bytes = pick_page_bytes(c, nch);
+  p.npw = MK_PAGES_BYTES / (MK_NC * p.page_bytes);
+  if (2 * c.hidden * 2 > p.page_bytes || p.page_bytes / (4 * c.hidden) > MK_GATE_SCRATCH) {
+    if (why) *why = "gate/up page geometry unsupported";
+    return MK_EINVAL;
+  }
+  p.s_max = std::max(1, std::min(n_cus / c.n_kv_heads, MK_ACT_FLOATS / (c.head_dim + 2)));
+  p.min_chunk = 256;
+  if (p.s_max < c.n_q_heads / c.n_kv_heads) {
+    if (why) *why = "too few CUs for one merger per query head of a group";
+    return MK_EINVAL;
+  }
+  const int d = c.hidden, nq = c.n_q_heads * c.head_dim, nqkv = nq + 2 * c.n_kv_heads * c.head_dim;
+  p.off.push_back(0);
+  for (int cu = 0; cu < n_cus; ++cu) {
+    int o0, on, q0, qn, f0, fn, v0, vn;
+    split(d, n_cus, cu, &o0, &on);
+    split(nqkv, n_cus, cu, &q0, &qn);
+    split(c.ffn, n_cus, cu, &f0, &fn);
+    split(c.vocab, n_cus, cu, &v0, &vn);
+    for (int l = 0; l < c.n_layers; ++l) {
+      MkInstr q = mk(MK_OP_QKV, l);
+      q.r0 = q0; q.n = qn; q.k0 = 0; q.kn = d; q.res_r0 = o0; q.res_n = on;
+      p.rec.push_back(q);
+      if (cu < c.n_kv_heads * p.s_max) {
+        MkInstr a = mk(MK_OP_ATTN, l);
+        a.a = cu / p.s_max;
+        a.b = cu % p.s_max;
+        p.rec.push_back(a);
+      }
+      if (on > 0) {
+        MkInstr o = mk(MK_OP_O, l);
+        o.r0 = o0; o.n = on; o.k0 = 0; o.kn = nq;
+        p.rec.push_back(o);
+      }
+      MkInstr gu = mk(MK_OP_GATEUP, l);
+      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d; gu.res_r0 = o0; gu.res_n = on;
+      p.rec.push_back(gu);
+      if (on > 0) {
+        for (int k = 0; k < nch; ++k) {
+          MkInstr dn = mk(MK_OP_DOWN, l);
+          dn.r0 = o0; dn.n = on; dn.kn = c.ffn / nch; dn.k0 = k * dn.kn; dn.a = k; dn.b = nch;
+          p.rec.push_back(dn);
+        }
+      }
+    }
+    MkInstr lm = mk(MK_OP_LMHEAD, c.n_layers);
+    lm.r0 = v0; lm.n = vn; lm.k0 = 0; lm.kn = d;
+    p.rec.push_back(lm);
+    p.off.push_back((int32_t)p.rec.size());
+  }
+  *out = std::move(p);
+  return MK_OK;
+}
