@@ -128,7 +128,7 @@ int mk_set_watchdog_us(mk_ctx* ctx, int64_t us);
 
 /* Schedule introspection (host only; valid after mk_load_weights or mk_plan_only).
  * mk_plan_info fills: [0] number of CUs planned, [1] instruction record size in
- * int32 words, [2] total records, [3] page bytes, [4] pages per compute wave,
+ * int32 words, [2] total records, [3] page bytes, [4] pages in the LDS ring,
  * [5] compute waves per CU, [6] attention splits per KV head, [7] LDS bytes.
  * mk_plan_copy copies `n_cus`+1 list offsets then the records (int32 words). */
 int mk_plan_info(const mk_ctx* ctx, int32_t info[8]);
@@ -145,6 +145,15 @@ int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out);
  * output [L][Hq*hd], SiLU(gate)*up [L][ffn], and the total word count; `host` may be
  * NULL to query the offsets only.  Errors: MK_ESTATE before mk_load_weights. */
 int mk_debug_dump(const mk_ctx* ctx, uint64_t* host, int64_t capacity_words, int64_t offsets[6]);
+
+/* Per-instruction timestamp trace (the time breakdown of one forward).  dev_buf is a
+ * borrowed device buffer of uint64 [n_cus][L][8] with L the longest per-CU instruction
+ * list; *required_words receives n_cus * L * 8 (pass dev_buf NULL to query, which also
+ * turns tracing off).  Every later step writes, per CU and instruction i, s_memrealtime
+ * ticks (100 MHz): [0] leader starts i, [1] its inputs are all present, [2] activation
+ * staged, [3] leader finished i (incl. attention merge / argmax), [4..7] compute wave
+ * 0..3 finished i.  Errors: MK_ESTATE before a schedule exists, MK_EINVAL if too small. */
+int mk_set_trace(mk_ctx* ctx, uint64_t* dev_buf, int64_t capacity_words, int64_t* required_words);
 
 /* Free everything the context allocated (not the borrowed weights or caches). */
 void mk_destroy(mk_ctx* ctx);

@@ -98,7 +98,7 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
     lm = sorted((r0, n) for r0, n, *_ in cover[(OPS["LMHEAD"], s.n_layers, 0)])
     assert sum(n for _, n in lm) == s.vocab and len(lm) == n_cus
     assert P["lds_bytes"] <= 160 * 1024
-    assert P["page_bytes"] * P["pages_per_wave"] * P["compute_waves"] <= 128 * 1024
+    assert P["page_bytes"] * P["ring_pages"] <= 128 * 1024
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama1b", "llama8b"])

@@ -3,6 +3,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -35,6 +36,8 @@ struct mk_ctx {
   unsigned long long* d_amax = nullptr;
   MkCtrl* d_ctrl = nullptr;
   int32_t* d_next = nullptr;   // argmax sink when the caller passes none
+  unsigned long long* trace = nullptr;   // borrowed device buffer, or null
+  int trace_len = 0;
 };
 
 namespace {
@@ -69,7 +72,7 @@ void free_device(mk_ctx* c) {
 }
 
 int reset_device_state(mk_ctx* c, hipStream_t s) {
-  HIPCHK(hipMemsetAsync(c->d_ll, 0, c->ll_words * sizeof(unsigned long long), s));
+  HIPCHK(hipMemsetAsync(c->d_ll, 0, (c->ll_words + MK_LL_PAD) * sizeof(unsigned long long), s));
   MkCtrl ctrl{};
   ctrl.epoch = 1;
   HIPCHK(hipMemcpyAsync(c->d_ctrl, &ctrl, sizeof(ctrl), hipMemcpyHostToDevice, s));
@@ -108,7 +111,7 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   p.attn_scale = (float)(1.0 / std::sqrt((double)g.head_dim));
   p.n_cus = c->plan.n_cus;
   p.page_bytes = c->plan.page_bytes;
-  p.npw = c->plan.npw;
+  p.nslot = c->plan.slots;
   p.lpp = c->plan.page_bytes / 1024;
   p.s_max = c->plan.s_max;
   p.min_chunk = c->plan.min_chunk;
@@ -133,6 +136,8 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   p.token = token;
   p.pos = pos;
   p.watchdog_ticks = c->watchdog_us * 100;   // s_memrealtime runs at 100 MHz
+  p.trace = c->trace;
+  p.trace_len = c->trace_len;
   void* args[] = {&p};
   HIPCHK(hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(c->plan.n_cus), dim3(MK_THREADS), args, 0,
                                     s));
@@ -265,7 +270,7 @@ int mk_load_weights(mk_ctx* c, const mk_weights* w) {
       (rc = alloc((void**)&c->d_off, c->plan.off.size() * sizeof(int32_t))) ||
       (rc = alloc((void**)&c->d_plan, c->plan.rec.size() * sizeof(MkInstr))) ||
       (rc = alloc((void**)&c->d_rope, rope.size() * sizeof(float))) ||
-      (rc = alloc((void**)&c->d_ll, c->ll_words * sizeof(unsigned long long))) ||
+      (rc = alloc((void**)&c->d_ll, (c->ll_words + MK_LL_PAD) * sizeof(unsigned long long))) ||
       (rc = alloc((void**)&c->d_amax, c->plan.n_cus * sizeof(unsigned long long))) ||
       (rc = alloc((void**)&c->d_ctrl, sizeof(MkCtrl))) || (rc = alloc((void**)&c->d_next, 64))) {
     free_device(c);
@@ -325,7 +330,7 @@ int mk_plan_info(const mk_ctx* c, int32_t info[8]) {
   info[1] = MK_INSTR_WORDS;
   info[2] = (int32_t)c->plan.rec.size();
   info[3] = c->plan.page_bytes;
-  info[4] = c->plan.npw;
+  info[4] = c->plan.slots;
   info[5] = MK_NC;
   info[6] = c->plan.s_max;
   info[7] = (int32_t)sizeof(mkdev::MkShared);
@@ -355,6 +360,24 @@ int mk_debug_dump(const mk_ctx* c, uint64_t* host, int64_t cap, int64_t offsets[
   HIPCHK(hipSetDevice(c->device));
   HIPCHK(hipDeviceSynchronize());
   HIPCHK(hipMemcpy(host, c->d_ll, c->ll_words * sizeof(uint64_t), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_set_trace(mk_ctx* c, uint64_t* dev_buf, int64_t capacity_words, int64_t* required_words) {
+  if (!c) return MK_EINVAL;
+  if (c->plan.off.empty()) return MK_ESTATE;
+  int len = 0;
+  for (size_t i = 0; i + 1 < c->plan.off.size(); ++i) len = std::max(len, c->plan.off[i + 1] - c->plan.off[i]);
+  const int64_t need = (int64_t)c->plan.n_cus * len * MK_TRACE_SLOTS;
+  if (required_words) *required_words = need;
+  if (!dev_buf) {
+    c->trace = nullptr;
+    c->trace_len = 0;
+    return MK_OK;
+  }
+  if (capacity_words < need || ((uintptr_t)dev_buf & 7)) return MK_EINVAL;
+  c->trace = (unsigned long long*)dev_buf;
+  c->trace_len = len;
   return MK_OK;
 }
 

@@ -6,13 +6,15 @@
 //  * Instruction interpreter.  Every CU walks its own ordered instruction list
 //    (QKV, ATTN, O, GATEUP, DOWN x4 per layer, then LMHEAD) laid out by the host.
 //  * Paged LDS with early weight loads.  The article pages shared memory so that the
-//    next instruction's weights load while the current one computes.  Here each of
-//    the MK_NC compute waves owns a ring of LDS pages and fills them with
-//    global_load_lds_dwordx4 (HBM -> LDS, no registers) for its future pages, across
-//    instruction boundaries and before the data an instruction depends on exists:
-//    weights and cached keys never depend on this step's activations.  A page is
-//    complete when the wave's vmcnt says so; the compiler is kept out of that
-//    accounting (it would otherwise wait for every DMA before any LDS access).
+//    next instruction's weights load while the current one computes.  Here MK_NL
+//    loader waves stream every page of the CU's list into one LDS ring with
+//    global_load_lds_dwordx4 (HBM -> LDS, no registers), across instruction
+//    boundaries and before the data an instruction depends on exists: weights and
+//    cached keys never depend on this step's activations.  A loader knows a page is
+//    complete from its own vmcnt and raises the slot's LDS flag; compute waves never
+//    issue loads, so a wait for data never stalls behind the weight stream.  The
+//    compiler is kept out of the DMA accounting (it would otherwise wait for every
+//    load before any LDS access).
 //  * Dependencies without grid barriers.  The article uses integer counters in
 //    global memory; on gfx950 the eight XCDs have separate L2s, so a counter costs a
 //    store-acknowledge, an atomic and a second round trip for the data.  Instead each
@@ -23,7 +25,7 @@
 //    (an atomic ticket, the one counter kept) advances the epoch for the next step.
 //  * A leader wave per CU does the waiting: it polls the inputs of the next
 //    instruction, applies RMSNorm / RoPE, stages the fp32 activation vector in LDS
-//    and releases the compute waves, which then only touch LDS.
+//    and releases the compute waves, which then only touch LDS and store results.
 //  * The article's 4-chunk MLP intermediate: the down projection is issued as 4
 //    K-chunks, each waiting only for its quarter of SiLU(gate)*up.
 //
@@ -56,12 +58,15 @@ typedef const int32_t* cint_t;
 
 struct __align__(16) MkShared {
   float act[MK_ACT_FLOATS];                 // staged activation vector of the instruction
-  char pages[MK_PAGES_BYTES];               // page rings, MK_NC x npw pages
+  char pages[MK_PAGES_BYTES];               // page ring (nslot pages)
   float xres[MK_MAX_RES_ROWS];              // x rows this CU's next residual adds to
   float rowacc[MK_MAX_RES_ROWS];            // DOWN partial sums over the K-chunks
   float rowres[MK_NC][64];                  // row results of the page being finished
   u64 amax[MK_NC];                          // per-wave argmax keys (LM head)
   int done[MK_NC];                          // instructions finished, per compute wave
+  uint16_t gain[MK_ACT_FLOATS];             // RMSNorm gains of the instruction being staged
+  int full[MK_MAX_SLOTS];                   // ring slot holds page k once full == k + 1
+  int freed[MK_MAX_SLOTS];                  // ring slot's page k consumed once freed == k + 1
   int act_seq;                              // instructions staged by the leader
   int abort_flag;
   uint32_t epoch;                           // tag of this step's words
@@ -112,6 +117,10 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// Ties a loaded value to this point of the program, so that the compiler cannot sink
+// the load into the branch that uses it (which would make one round trip per load).
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ int lds_load(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -154,17 +163,42 @@ __device__ __forceinline__ float dot8(uint4 w, const float* a, float acc) {
   return acc;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+// ------------------------------------------------------------------ reductions (DPP)
+// Cross-lane sums through DPP moves (no LDS round trip).  sumN leaves the sum of each
+// aligned group of N lanes in every lane of the group.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v, float old) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<0xB1>(v, 0.f);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v, 0.f);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v, 0.f);   // row_half_mirror
   return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += dpp_f<0x140>(v, 0.f);   // row_mirror
+  return v;
+}
+// Sum over the wave, returned wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  v += dpp_f<0x142, 0xa>(v, 0.f);   // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xc>(v, 0.f);   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x4E>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x141>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x140>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x142, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x143, 0xc>(v, -INFINITY));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-// Sum within aligned groups of g lanes (g a power of two <= 64).
+// Sum within aligned groups of g lanes (g a power of two <= 64), by lane swaps.
 __device__ __forceinline__ float group_sum(float v, int g) {
   for (int off = g >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
@@ -183,6 +217,11 @@ __device__ __forceinline__ u64 amax_key(float v, uint32_t idx) {
   uint32_t u = __float_as_uint(v);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((u64)u << 32) | (u64)(0xffffffffu - idx);
+}
+
+__device__ __forceinline__ void trace_mark(const MkParams& p, int cu, int i, int slot, int lane) {
+  if (p.trace && lane == 0 && i < p.trace_len)
+    p.trace[((size_t)cu * p.trace_len + i) * MK_TRACE_SLOTS + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
 // ------------------------------------------------------------------ step geometry
@@ -211,75 +250,121 @@ __device__ __forceinline__ void attn_range(const StepGeo& g, int s, int* j0, int
   *cached_end = min(*j1, g.pos);
 }
 
-__device__ __forceinline__ int rows_per_page(const MkParams& p, const MkInstr& in) {
-  const int seg = 2 * in.kn;
-  return in.op == MK_OP_GATEUP ? p.page_bytes / (2 * seg) : p.page_bytes / seg;
-}
+// An instruction decoded once: everything its pages need, wave-uniform.
+struct Dec {
+  int op, layer, r0, n, k0, kn, a, b;
+  int np;            // pages of the instruction on this CU
+  int seg;           // bytes of one row segment
+  int rpp;           // rows per page (GATEUP: gate/up pairs per page)
+  int upr;           // 1 KiB units per row, or 0 when a row is shorter than 1 KiB
+  int lpr_sh;        // log2(lanes per row) when a row is shorter than 1 KiB
+  int s1, s2;        // QKV: rows below s1 come from m0, below s2 from m1, the rest from m2
+  const char* m0;    // row 0 of each source matrix, input column k0 applied (bytes)
+  const char* m1;
+  const char* m2;
+  long long stride;  // bytes between rows
+  int j0, ce;        // ATTN: cached keys [j0, ce); m0 / m1 = K / V of (layer, kv head) at key 0
+};
 
-__device__ __forceinline__ int instr_pages(const MkParams& p, const MkInstr& in, const StepGeo& g) {
+__device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, const StepGeo& g) {
+  Dec d;
+  d.op = in.op; d.layer = in.layer; d.r0 = in.r0; d.n = in.n; d.k0 = in.k0; d.kn = in.kn; d.a = in.a; d.b = in.b;
+  d.s1 = d.s2 = 0;
+  d.m0 = d.m1 = d.m2 = nullptr;
+  d.upr = d.lpr_sh = 0;
+  d.seg = d.rpp = 0;
+  d.j0 = d.ce = 0;
+  d.stride = 0;
   if (in.op == MK_OP_ATTN) {
-    if (in.b >= g.s_eff) return 0;
-    int j0, j1, ce;
-    attn_range(g, in.b, &j0, &j1, &ce);
-    const int cached = ce - j0;
-    return cached > 0 ? (cached + g.ppp - 1) / g.ppp : 0;
-  }
-  const int rpp = rows_per_page(p, in);
-  return (in.n + rpp - 1) / rpp;
-}
-
-__device__ __forceinline__ const uint16_t* row_ptr(const MkParams& p, const MkInstr& in, int row) {
-  const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
-  switch (in.op) {
-    case MK_OP_QKV:
-      if (row < p.nq) return L.wq + (size_t)row * p.d;
-      if (row < p.nq + p.nkv) return L.wk + (size_t)(row - p.nq) * p.d;
-      return L.wv + (size_t)(row - p.nq - p.nkv) * p.d;
-    case MK_OP_O: return L.wo + (size_t)row * p.nq;
-    case MK_OP_DOWN: return L.wd + (size_t)row * p.F;
-    default: return p.lm_head + (size_t)row * p.d;   // MK_OP_LMHEAD
-  }
-}
-
-// Issue the DMA of page `pg` of instruction `in` into the LDS page at `slot`: always
-// p.lpp load instructions of 1 KiB, so that vmcnt accounting is a multiple of lpp.
-// Lanes beyond the page payload re-read the page's first 16 bytes (always valid).
-__device__ __forceinline__ void issue_page(const MkParams& p, const MkInstr& in, int pg,
-                                           const StepGeo& g, uint32_t slot, int lane) {
-  if (in.op == MK_OP_ATTN) {
-    int j0, j1, ce;
-    attn_range(g, in.b, &j0, &j1, &ce);
-    const int q0 = j0 + pg * g.ppp;
-    const int np = min(g.ppp, ce - q0);
-    const int rowb = 2 * p.hd;
-    const int kbytes = np * rowb;
+    d.np = 0;
+    if (in.b < g.s_eff) {
+      int j1;
+      attn_range(g, in.b, &d.j0, &j1, &d.ce);
+      const int cached = d.ce - d.j0;
+      d.np = cached > 0 ? (cached + g.ppp - 1) / g.ppp : 0;
+    }
     const size_t head = ((size_t)(in.layer * 2) * p.hkv + in.a) * p.max_ctx;
-    const char* kb = (const char*)(p.kv + (head + q0) * p.hd);
-    const char* vb = (const char*)(p.kv + (head + (size_t)p.hkv * p.max_ctx + q0) * p.hd);
-    for (int u = 0; u < p.lpp; ++u) {
+    d.m0 = (const char*)(p.kv + head * p.hd);
+    d.m1 = (const char*)(p.kv + (head + (size_t)p.hkv * p.max_ctx) * p.hd);
+    return d;
+  }
+  d.seg = 2 * in.kn;
+  d.rpp = in.op == MK_OP_GATEUP ? p.page_bytes / (2 * d.seg) : p.page_bytes / d.seg;
+  d.np = (in.n + d.rpp - 1) / d.rpp;
+  if (d.seg >= 1024) d.upr = d.seg >> 10;
+  else d.lpr_sh = 31 - __builtin_clz((unsigned)(d.seg >> 4));
+  const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
+  // Plain selects, not a switch: a switch over runtime values becomes a table in
+  // private memory, read with vector loads.
+  const bool qkv = in.op == MK_OP_QKV, gu = in.op == MK_OP_GATEUP, o = in.op == MK_OP_O,
+             dn = in.op == MK_OP_DOWN;
+  const uint16_t* a0 = qkv ? L.wq : gu ? L.wg : o ? L.wo : dn ? L.wd : p.lm_head;
+  const uint16_t* a1 = qkv ? L.wk : gu ? L.wu : nullptr;
+  const uint16_t* a2 = qkv ? L.wv : nullptr;
+  d.stride = 2LL * (o ? p.nq : dn ? p.F : p.d);
+  if (qkv) {
+    d.s1 = p.nq;
+    d.s2 = p.nq + p.nkv;
+  }
+  d.m0 = (const char*)(a0 + in.k0);
+  d.m1 = a1 ? (const char*)(a1 + in.k0) : d.m0;
+  d.m2 = a2 ? (const char*)(a2 + in.k0) : d.m0;
+  return d;
+}
+
+// Row j of page `first`: the page holds rows first.. of the instruction, or for GATEUP the
+// interleaved pairs gate(f), up(f), gate(f+1), up(f+1), ... with f = r0 + first.
+__device__ __forceinline__ const char* page_row(const Dec& d, int first, int j) {
+  if (d.op == MK_OP_GATEUP) {
+    const long long f = d.r0 + first + (j >> 1);
+    return ((j & 1) ? d.m1 : d.m0) + f * d.stride;
+  }
+  const int gr = d.r0 + first + j;
+  if (d.op == MK_OP_QKV) {
+    if (gr >= d.s2) return d.m2 + (long long)(gr - d.s2) * d.stride;
+    if (gr >= d.s1) return d.m1 + (long long)(gr - d.s1) * d.stride;
+  }
+  return d.m0 + (long long)gr * d.stride;
+}
+
+// Issue the DMA of page pg into the LDS page at `slot`: always `lpp` loads of 1 KiB so
+// the wave's vmcnt moves in multiples of lpp; loads past the payload re-read valid bytes.
+__device__ __forceinline__ void issue_page(const Dec& d, int pg, int ppp, int hd, int lpp, uint32_t slot,
+                                           int lane) {
+  if (d.op == MK_OP_ATTN) {
+    const int q0 = d.j0 + pg * ppp;
+    const int np = min(ppp, d.ce - q0);
+    const int rowb = 2 * hd;
+    const int kbytes = np * rowb;
+    const char* kb = d.m0 + (size_t)q0 * rowb;
+    const char* vb = d.m1 + (size_t)q0 * rowb;
+    for (int u = 0; u < lpp; ++u) {
       const int o = u * 1024 + lane * 16;
       const char* a = o < kbytes ? kb + o : (o < 2 * kbytes ? vb + (o - kbytes) : kb);
       dma16(a, slot + u * 1024);
     }
     return;
   }
-  const int seg = 2 * in.kn;
-  const int rpp = rows_per_page(p, in);
-  const int first = pg * rpp;
-  const int m = min(rpp, in.n - first);                 // rows (GATEUP: pairs) in the page
-  const int payload = (in.op == MK_OP_GATEUP ? 2 * m : m) * seg;
-  const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
-  for (int u = 0; u < p.lpp; ++u) {
-    int o = u * 1024 + lane * 16;
-    if (o >= payload) o = 0;
-    const int j = o / seg;
-    const int cb = o - j * seg;
-    const uint16_t* rp;
-    if (in.op == MK_OP_GATEUP)
-      rp = j < m ? L.wg + (size_t)(in.r0 + first + j) * p.d : L.wu + (size_t)(in.r0 + first + j - m) * p.d;
-    else
-      rp = row_ptr(p, in, in.r0 + first + j);
-    dma16((const char*)(rp + in.k0) + cb, slot + u * 1024);
+  const int first = pg * d.rpp;
+  const int m = min(d.rpp, d.n - first);
+  const int rows = d.op == MK_OP_GATEUP ? 2 * m : m;
+  if (d.upr) {
+    // One row base per row (a few scalar ops), then its 1 KiB units by plain adds.
+    uint32_t dst = slot;
+    int u = 0;
+    for (int j = 0; j < rows; ++j) {
+      const char* rb = page_row(d, first, j) + lane * 16;
+      for (int c = 0; c < d.upr; ++c, ++u, dst += 1024) dma16(rb + c * 1024, dst);
+    }
+    const char* dummy = d.m0 + lane * 16;   // keeps the load count at lpp
+    for (; u < lpp; ++u, dst += 1024) dma16(dummy, dst);
+  } else {
+    const int rpu = 64 >> d.lpr_sh;
+    const int cl = lane & ((1 << d.lpr_sh) - 1);
+    for (int u = 0; u < lpp; ++u) {
+      const int jl = u * rpu + (lane >> d.lpr_sh);
+      dma16(page_row(d, first, jl < rows ? jl : 0) + cl * 16, slot + u * 1024);
+    }
   }
 }
 
@@ -332,87 +417,204 @@ __device__ __forceinline__ bool wait_all_done(const MkParams& p, MkShared& sh, i
   return true;
 }
 
-// ------------------------------------------------------------------ compute waves
-// Finish one GEMV page: dot every row of the page with the staged activation.
-__device__ __forceinline__ void gemv_page(const MkParams& p, MkShared& sh, const MkInstr& in, int pg,
-                                          const char* page, int w, int lane, uint32_t epoch,
-                                          u64* best) {
-  const int seg = 2 * in.kn;
-  const int rpp = rows_per_page(p, in);
-  const int first = pg * rpp;
-  const int m = min(rpp, in.n - first);
-  const int nrows = in.op == MK_OP_GATEUP ? 2 * m : m;
-  float* res = sh.rowres[w];
-  if (seg >= 1024) {
-    const int upr = seg >> 10;
-    for (int r = 0; r < nrows; ++r) {
-      float acc = 0.f;
-      for (int u = 0; u < upr; ++u) {
-        const uint4 wv = *(const uint4*)(page + (r * upr + u) * 1024 + lane * 16);
-        acc = dot8(wv, sh.act + u * 512 + lane * 8, acc);
+// ------------------------------------------------------------------ page ring
+// The pages of the CU's whole list, in list order, are numbered k = 0, 1, ...; page k
+// lives in ring slot k % nslot, is issued by loader wave k % MK_NL and consumed by
+// compute wave k % MK_NC.  LDS flags: full[slot] = k + 1 once page k has landed,
+// freed[slot] = k + 1 once its compute wave has read it.  nslot is a multiple of
+// MK_NL, so the page a loader waits to be freed is one it issued itself.
+__device__ __forceinline__ int first_of(int who, int base, int period) {
+  return ((who - base) % period + period) % period;
+}
+
+// Loader wave l.  It publishes its pages in order, each once vmcnt shows it complete,
+// keeping at most D of them unpublished (vmcnt counts to 63).  While it waits for a
+// slot still in use it keeps publishing what it has in flight: a compute wave may be
+// waiting for one of those pages.
+__device__ __forceinline__ void loader_wave(const MkParams& p, MkShared& sh, cinstr_t list, int nins,
+                                            const StepGeo& g, int l, int lane) {
+  const int nslot = p.nslot, lpp = p.lpp, pb = p.page_bytes;
+  const uint32_t ring = lds_addr(sh.pages);
+  const int D = min(8, min(nslot / MK_NL, 63 / lpp + 1));
+  int oldest = 0, pend = 0;   // own pages issued and not yet published: oldest, then every MK_NL-th
+  int base = 0;
+  for (int i = 0; i < nins; ++i) {
+    const Dec d = decode(p, list[i], g);
+    lane = opaque(lane);
+    for (int pg = first_of(l, base, MK_NL); pg < d.np; pg += MK_NL) {
+      const int k = base + pg;
+      const int slot = k % nslot;
+      // Slot still in use: publish own pages as they land (oldest first) while waiting.
+      while (lds_load(&sh.freed[slot]) < k - nslot + 1) {
+        if (pend == 0) {
+          if (!wait_flag(p, sh, &sh.freed[slot], k - nslot + 1, false)) {
+            wait_vmcnt(0);   // nothing may land in LDS after the wave has left
+            return;
+          }
+          break;
+        }
+        wait_vmcnt((pend - 1) * lpp);
+        if (lane == 0) lds_store(&sh.full[oldest % nslot], oldest + 1);
+        oldest += MK_NL;
+        --pend;
       }
-      acc = wave_sum(acc);
-      if (lane == 0) res[r] = acc;
+      issue_page(d, pg, g.ppp, p.hd, lpp, ring + (uint32_t)(slot * pb), lane);
+      if (pend == 0) oldest = k;
+      ++pend;
+      if (pend == D) {   // the oldest is complete once at most (D - 1) pages are outstanding
+        wait_vmcnt((D - 1) * lpp);
+        if (lane == 0) lds_store(&sh.full[oldest % nslot], oldest + 1);
+        oldest += MK_NL;
+        --pend;
+      }
     }
-  } else {
-    const int lpr = seg >> 4;             // lanes per row
-    const int rpu = 64 / lpr;             // rows per 1 KiB unit
-    const int c = lane & (lpr - 1);
-    for (int u = 0; u * rpu < nrows; ++u) {
-      const uint4 wv = *(const uint4*)(page + u * 1024 + lane * 16);
-      float acc = dot8(wv, sh.act + c * 8, 0.f);
-      acc = group_sum(acc, lpr);
-      const int r = u * rpu + lane / lpr;
-      if (c == 0 && r < nrows) res[r] = acc;
-    }
+    base += d.np;
   }
+  wait_vmcnt(0);
+  for (; pend > 0; --pend, oldest += MK_NL)
+    if (lane == 0) lds_store(&sh.full[oldest % nslot], oldest + 1);
+}
+
+// Page k for a compute wave, once it has landed (nullptr if the wait was abandoned).
+__device__ __forceinline__ const char* page_wait(const MkParams& p, MkShared& sh, int k) {
+  const int slot = k % p.nslot;
+  if (!wait_flag(p, sh, &sh.full[slot], k + 1, false)) return nullptr;
+  return sh.pages + slot * p.page_bytes;
+}
+// The wave has finished reading page k: once its LDS reads have returned the loader
+// may overwrite the slot.
+__device__ __forceinline__ void page_free(const MkParams& p, MkShared& sh, int k, int lane) {
   lds_fence();
-  // Epilogue: lane j finishes row (or gate/up pair) j of the page.
-  const int l = in.layer;
-  const int j = lane;
-  if (j >= m) return;
-  const int row = in.r0 + first + j;
-  switch (in.op) {
-    case MK_OP_QKV: {
-      // group-major: [kv head g][q heads of g | k_g | v_g][hd]
-      const int grp = (p.hpg + 2) * p.hd;
-      int idx;
-      if (row < p.nq) {
-        const int h = row / p.hd;
-        idx = (h / p.hpg) * grp + (h % p.hpg) * p.hd + (row - h * p.hd);
-      } else if (row < p.nq + p.nkv) {
-        const int r = row - p.nq;
-        idx = (r / p.hd) * grp + p.hpg * p.hd + (r % p.hd);
-      } else {
-        const int r = row - p.nq - p.nkv;
-        idx = (r / p.hd) * grp + (p.hpg + 1) * p.hd + (r % p.hd);
-      }
-      ll_store(p.ll_qkv + (size_t)l * p.nqkv + idx, res[j], epoch);
+  if (lane == 0) lds_store(&sh.freed[k % p.nslot], k + 1);
+}
+
+// ------------------------------------------------------------------ compute waves
+// Group-major index of a raw q/k/v row: [kv head][q heads of the group | k | v][hd].
+__device__ __forceinline__ int qkv_index(const MkParams& p, int row) {
+  const int grp = (p.hpg + 2) * p.hd;
+  if (row < p.nq) {
+    const int h = row / p.hd;
+    return (h / p.hpg) * grp + (h % p.hpg) * p.hd + (row - h * p.hd);
+  }
+  if (row < p.nq + p.nkv) {
+    const int r = row - p.nq;
+    return (r / p.hd) * grp + p.hpg * p.hd + (r % p.hd);
+  }
+  const int r = row - p.nq - p.nkv;
+  return (r / p.hd) * grp + (p.hpg + 1) * p.hd + (r % p.hd);
+}
+
+// Finish one output row (value v, uniform over the wave; lane 0 stores).
+__device__ __forceinline__ void row_epilogue(const MkParams& p, MkShared& sh, const Dec& d, int gr, float v,
+                                             int lane, uint32_t epoch, u64* best) {
+  const int l = d.layer;
+  switch (d.op) {
+    case MK_OP_QKV:
+      if (lane == 0) ll_store(p.ll_qkv + (size_t)l * p.nqkv + qkv_index(p, gr), v, epoch);
       break;
-    }
     case MK_OP_O:
-      ll_store(p.ll_x + (size_t)(2 * l + 1) * p.d + row, sh.xres[row - in.r0] + res[j], epoch);
+      if (lane == 0) ll_store(p.ll_x + (size_t)(2 * l + 1) * p.d + gr, sh.xres[gr - d.r0] + v, epoch);
       break;
-    case MK_OP_GATEUP: {
-      const float gt = res[j], up = res[m + j];
-      const float a = (gt / (1.0f + __expf(-gt))) * up;
-      ll_store(p.ll_a + (size_t)l * p.F + row, a, epoch);
-      break;
-    }
     case MK_OP_DOWN: {
-      const int k = row - in.r0;
-      const float acc = (in.a == 0 ? 0.f : sh.rowacc[k]) + res[j];
-      if (in.a + 1 < in.b) sh.rowacc[k] = acc;
-      else ll_store(p.ll_x + (size_t)(2 * l + 2) * p.d + row, sh.xres[k] + acc, epoch);
+      const int k = gr - d.r0;
+      const float acc = (d.a == 0 ? 0.f : sh.rowacc[k]) + v;
+      if (d.a + 1 < d.b) {
+        if (lane == 0) sh.rowacc[k] = acc;
+      } else if (lane == 0) {
+        ll_store(p.ll_x + (size_t)(2 * l + 2) * p.d + gr, sh.xres[k] + acc, epoch);
+      }
       break;
     }
     default: {  // MK_OP_LMHEAD
-      p.logits[row] = res[j];
-      const u64 key = amax_key(res[j], (uint32_t)row);
+      if (lane == 0) p.logits[gr] = v;
+      const u64 key = amax_key(v, (uint32_t)gr);
       if (key > *best) *best = key;
       break;
     }
   }
+}
+
+__device__ __forceinline__ void gateup_epilogue(const MkParams& p, const Dec& d, int f, float gt, float up,
+                                                int lane, uint32_t epoch) {
+  const float a = (gt / (1.0f + __expf(-gt))) * up;
+  if (lane == 0) ll_store(p.ll_a + (size_t)d.layer * p.F + f, a, epoch);
+}
+
+// Rows of at least 1 KiB: the lane's slice of the activation stays in registers for the
+// whole instruction; each row is UPR units of 1 KiB, lane l holding bytes 16l.. of each.
+template <int UPR>
+__device__ __forceinline__ float row_dot(const char* page, int j, const float (&av)[UPR][8], int lane) {
+  uint4 wv[UPR];   // all units' LDS reads first, so their latency overlaps
+#pragma unroll
+  for (int u = 0; u < UPR; ++u) wv[u] = *(const uint4*)(page + (j * UPR + u) * 1024 + lane * 16);
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < UPR; ++u) acc = dot8(wv[u], av[u], acc);
+  return acc;
+}
+
+template <int UPR>
+__device__ __forceinline__ bool gemv_wide(const MkParams& p, MkShared& sh, const Dec& d, int base, int w, int lane,
+                                          uint32_t epoch, u64* best) {
+  float av[UPR][8];
+#pragma unroll
+  for (int u = 0; u < UPR; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) av[u][e] = sh.act[u * 512 + lane * 8 + e];
+  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
+    const char* page = page_wait(p, sh, base + pg);
+    if (!page) return false;
+    const int first = pg * d.rpp;
+    const int m = min(d.rpp, d.n - first);
+    if (d.op == MK_OP_GATEUP) {
+      for (int j = 0; j < m; ++j) {
+        const float g = wave_sum(row_dot<UPR>(page, 2 * j, av, lane));
+        const float u = wave_sum(row_dot<UPR>(page, 2 * j + 1, av, lane));
+        gateup_epilogue(p, d, d.r0 + first + j, g, u, lane, epoch);
+      }
+    } else {
+      int j = 0;
+      for (; j + 1 < m; j += 2) {
+        const float v0 = wave_sum(row_dot<UPR>(page, j, av, lane));
+        const float v1 = wave_sum(row_dot<UPR>(page, j + 1, av, lane));
+        row_epilogue(p, sh, d, d.r0 + first + j, v0, lane, epoch, best);
+        row_epilogue(p, sh, d, d.r0 + first + j + 1, v1, lane, epoch, best);
+      }
+      if (j < m) row_epilogue(p, sh, d, d.r0 + first + j, wave_sum(row_dot<UPR>(page, j, av, lane)), lane, epoch, best);
+    }
+    page_free(p, sh, base + pg, lane);
+  }
+  return true;
+}
+
+// Rows shorter than 1 KiB (small models): several rows per 1 KiB unit, lpr lanes per row;
+// results go through LDS so that lane j can finish row j.
+__device__ __forceinline__ bool gemv_narrow(const MkParams& p, MkShared& sh, const Dec& d, int base, int w,
+                                            int lane, uint32_t epoch, u64* best) {
+  const int lpr = 1 << d.lpr_sh, rpu = 64 >> d.lpr_sh, c = lane & (lpr - 1);
+  float av[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) av[e] = sh.act[c * 8 + e];
+  float* res = sh.rowres[w];
+  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
+    const char* page = page_wait(p, sh, base + pg);
+    if (!page) return false;
+    const int first = pg * d.rpp;
+    const int m = min(d.rpp, d.n - first);
+    const int rows = d.op == MK_OP_GATEUP ? 2 * m : m;
+    for (int u = 0; u * rpu < rows; ++u) {
+      float acc = dot8(*(const uint4*)(page + u * 1024 + lane * 16), av, 0.f);
+      acc = group_sum(acc, lpr);
+      const int j = u * rpu + (lane >> d.lpr_sh);
+      if (c == 0 && j < rows) res[j] = acc;
+    }
+    page_free(p, sh, base + pg, lane);
+    for (int j = 0; j < m; ++j) {
+      if (d.op == MK_OP_GATEUP) gateup_epilogue(p, d, d.r0 + first + j, res[2 * j], res[2 * j + 1], lane, epoch);
+      else row_epilogue(p, sh, d, d.r0 + first + j, res[j], lane, epoch, best);
+    }
+  }
+  return true;
 }
 
 template <int HD, int HPG>
@@ -438,7 +640,8 @@ __device__ __forceinline__ void attn_init(AttnState<HD, HPG>& st, const MkShared
   }
 }
 
-// One page of cached keys/values: [npos][HD] keys, then [npos][HD] values.
+// One page of cached keys/values: [npos][HD] keys, then [npos][HD] values.  Lane l holds
+// 8 dims (chunk l % LPP) of position l / LPP of each 1 KiB unit.
 template <int HD, int HPG>
 __device__ __forceinline__ void attn_page(AttnState<HD, HPG>& st, const char* page, int npos, float scale,
                                           int lane) {
@@ -459,7 +662,7 @@ __device__ __forceinline__ void attn_page(AttnState<HD, HPG>& st, const char* pa
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
         float part = dot8(kw, st.q[h], 0.f);
-        part = group_sum(part, LPP);
+        part = LPP == 8 ? sum8(part) : sum16(part);
         s[u][h] = valid ? part * scale : -INFINITY;
       }
     }
@@ -494,176 +697,137 @@ __device__ __forceinline__ void attn_page(AttnState<HD, HPG>& st, const char* pa
   }
 }
 
-// Reduce the wave's state over its position groups and leave (m, l, o) in LDS.
+// Reduce the wave's state over its position groups and leave (m, l, o) in LDS.  The
+// HPG * 9 sums are independent: each swap step is applied to all of them before the
+// next, so their LDS round trips overlap instead of forming one long chain.
 template <int HD, int HPG>
 __device__ __forceinline__ void attn_publish(AttnState<HD, HPG>& st, MkShared& sh, int w, int lane) {
   constexpr int LPP = HD / 8;
   float* part = sh.act + MK_PART_OFF + w * HPG * (HD + 2);
 #pragma unroll
+  for (int off = LPP; off < 64; off <<= 1) {
+    float t[HPG][9];
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      t[h][8] = __shfl_xor(st.l[h], off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[h][e] = __shfl_xor(st.o[h][e], off);
+    }
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      st.l[h] += t[h][8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.o[h][e] += t[h][e];
+    }
+  }
+#pragma unroll
   for (int h = 0; h < HPG; ++h) {
-    float l = st.l[h];
+    if (lane < LPP) {
 #pragma unroll
-    for (int off = LPP; off < 64; off <<= 1) l += __shfl_xor(l, off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = st.o[h][e];
-#pragma unroll
-      for (int off = LPP; off < 64; off <<= 1) v += __shfl_xor(v, off);
-      if (lane < LPP) part[h * (HD + 2) + 2 + lane * 8 + e] = v;
+      for (int e = 0; e < 8; ++e) part[h * (HD + 2) + 2 + lane * 8 + e] = st.o[h][e];
     }
     if (lane == 0) {
       part[h * (HD + 2)] = st.m[h];
-      part[h * (HD + 2) + 1] = l;
+      part[h * (HD + 2) + 1] = st.l[h];
     }
   }
 }
 
-
-// ------------------------------------------------------------------ page ring
-// The stream of pages one compute wave consumes, in consumption order.  Page pg of
-// instruction i goes to wave (base_i + pg) % MK_NC, base_i = pages of instructions
-// before i, so successive instructions start on successive waves.
-__device__ __forceinline__ int first_page(int w, int base) { return ((w - base) % MK_NC + MK_NC) % MK_NC; }
-
-struct Ring {
-  const MkParams* p;
-  cinstr_t list;
-  int nins;
-  StepGeo g;
-  int w, lane;
-  const char* base;       // this wave's pages (LDS)
-  uint32_t base_lds;
-  int issued, consumed;
-  int si, spg, sbase, snp;  // issue cursor: instruction, page, pages before it, its pages
-
-  __device__ __forceinline__ void settle() {
-    while (si < nins && spg >= snp) {
-      sbase += snp;
-      ++si;
-      if (si < nins) {
-        snp = instr_pages(*p, list[si], g);
-        spg = first_page(w, sbase);
-      }
-    }
-  }
-  __device__ __forceinline__ void init() {
-    issued = consumed = 0;
-    si = 0;
-    sbase = 0;
-    snp = nins > 0 ? instr_pages(*p, list[0], g) : 0;
-    spg = first_page(w, 0);
-    settle();
-    for (int k = 0; k < p->npw; ++k) issue();
-  }
-  __device__ __forceinline__ void issue() {
-    if (si >= nins) return;
-    issue_page(*p, list[si], spg, g, base_lds + (uint32_t)((issued % p->npw) * p->page_bytes), lane);
-    ++issued;
-    spg += MK_NC;
-    settle();
-  }
-  // Oldest page in flight, once it has landed.
-  __device__ __forceinline__ const char* front() {
-    wait_vmcnt((issued - consumed - 1) * p->lpp);
-    return base + (consumed % p->npw) * p->page_bytes;
-  }
-  __device__ __forceinline__ void pop() {
-    ++consumed;
-    issue();
-  }
-};
-
 template <int HD, int HPG>
-__device__ __forceinline__ void attn_run(const MkParams& p, MkShared& sh, const MkInstr& in, int np, int p0,
-                                         Ring& r, int w, int lane) {
+__device__ __forceinline__ bool attn_run(const MkParams& p, MkShared& sh, const Dec& d, const StepGeo& g, int base,
+                                         int w, int lane) {
   AttnState<HD, HPG> st;
   attn_init<HD, HPG>(st, sh, lane);
-  int j0, j1, ce;
-  attn_range(r.g, in.b, &j0, &j1, &ce);
-  for (int pg = p0; pg < np; pg += MK_NC) {
-    const char* page = r.front();
-    const int npos = min(r.g.ppp, ce - (j0 + pg * r.g.ppp));
+  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
+    const char* page = page_wait(p, sh, base + pg);
+    if (!page) return false;
+    const int npos = min(g.ppp, d.ce - (d.j0 + pg * g.ppp));
     attn_page<HD, HPG>(st, page, npos, p.attn_scale, lane);
-    r.pop();
+    page_free(p, sh, base + pg, lane);
   }
   attn_publish<HD, HPG>(st, sh, w, lane);
+  return true;
 }
 
 __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared& sh, cinstr_t list, int nins,
-                             const StepGeo& g, int w, int lane, uint32_t epoch) {
-  Ring r;
-  r.p = &p;
-  r.list = list;
-  r.nins = nins;
-  r.g = g;
-  r.w = w;
-  r.lane = lane;
-  r.base = sh.pages + w * p.npw * p.page_bytes;
-  r.base_lds = lds_addr(r.base);
-  r.init();
-  int cbase = 0;
+                                             const StepGeo& g, int w, int lane, uint32_t epoch) {
+  int base = 0;   // ring number of the instruction's first page
   for (int i = 0; i < nins; ++i) {
-    const MkInstr in = list[i];
+    const Dec d = decode(p, list[i], g);
     lane = opaque(lane);
-    r.lane = lane;
-    const int np = instr_pages(p, in, g);
-    const int p0 = first_page(w, cbase);
-    cbase += np;
-    if (!wait_flag(p, sh, &sh.act_seq, i + 1, false)) break;
-    if (in.op == MK_OP_ATTN) {
+    if (!wait_flag(p, sh, &sh.act_seq, i + 1, false)) return;
+    bool ok = true;
+    if (d.op == MK_OP_ATTN) {
       // A split that is inactive at this position does nothing: in particular it must not
       // write partials into act, which other waves may still read for the previous
       // instruction (the leader releases inactive splits without waiting for them).
-      if (in.b >= g.s_eff) {
+      if (d.b >= g.s_eff) {
       } else if (p.hd == 64) {
-        if (p.hpg == 4) attn_run<64, 4>(p, sh, in, np, p0, r, w, lane);
-        else if (p.hpg == 2) attn_run<64, 2>(p, sh, in, np, p0, r, w, lane);
-        else attn_run<64, 1>(p, sh, in, np, p0, r, w, lane);
+        if (p.hpg == 4) ok = attn_run<64, 4>(p, sh, d, g, base, w, lane);
+        else if (p.hpg == 2) ok = attn_run<64, 2>(p, sh, d, g, base, w, lane);
+        else ok = attn_run<64, 1>(p, sh, d, g, base, w, lane);
       } else {
-        if (p.hpg == 4) attn_run<128, 4>(p, sh, in, np, p0, r, w, lane);
-        else if (p.hpg == 2) attn_run<128, 2>(p, sh, in, np, p0, r, w, lane);
-        else attn_run<128, 1>(p, sh, in, np, p0, r, w, lane);
+        if (p.hpg == 4) ok = attn_run<128, 4>(p, sh, d, g, base, w, lane);
+        else if (p.hpg == 2) ok = attn_run<128, 2>(p, sh, d, g, base, w, lane);
+        else ok = attn_run<128, 1>(p, sh, d, g, base, w, lane);
       }
     } else {
       u64 best = 0;
-      for (int pg = p0; pg < np; pg += MK_NC) {
-        const char* page = r.front();
-        gemv_page(p, sh, in, pg, page, w, lane, epoch, &best);
-        r.pop();
+      switch (d.upr) {
+        case 0: ok = gemv_narrow(p, sh, d, base, w, lane, epoch, &best); break;
+        case 1: ok = gemv_wide<1>(p, sh, d, base, w, lane, epoch, &best); break;
+        case 2: ok = gemv_wide<2>(p, sh, d, base, w, lane, epoch, &best); break;
+        case 4: ok = gemv_wide<4>(p, sh, d, base, w, lane, epoch, &best); break;
+        case 7: ok = gemv_wide<7>(p, sh, d, base, w, lane, epoch, &best); break;
+        default: ok = gemv_wide<8>(p, sh, d, base, w, lane, epoch, &best); break;
       }
-      if (in.op == MK_OP_LMHEAD) {
+      if (d.op == MK_OP_LMHEAD) {
         best = wave_max_u64(best);
         if (lane == 0) sh.amax[w] = best;
       }
     }
+    if (!ok) return;
+    base += d.np;
     lds_fence();
     if (lane == 0) lds_store(&sh.done[w], i + 1);
+    trace_mark(p, blockIdx.x, i, 4 + w, lane);
   }
-  wait_vmcnt(0);   // no page load may land after the wave has left
 }
 
 // ------------------------------------------------------------------ leader wave
+// Loads in the leader are issued in batches with no branch between them: a load under
+// a per-lane condition gets its own block, and the compiler then waits for each one
+// before the next (a full round trip per load).  Out-of-range lanes load a valid
+// address and discard the value.
+
 // Poll words [base, base + 64*MK_GATHER_MAXW) of src until all carry this step's
-// epoch.  Word base + 64k + lane lands in wv[k].
+// epoch.  Word base + 64k + lane lands in wv[k]; words past `total` are loaded (the
+// arena is padded by MK_LL_PAD words) but not waited for.
+// The first pass loads every word; while words are missing, each lane re-polls only its
+// first missing word (one load per lane per round trip) and the wave reloads the whole
+// batch once one has arrived: re-polling whole vectors from every CU would compete with
+// the weight stream for HBM.  Reloading a word that already carries the epoch is
+// harmless: each word is written once per step, and a later load of a location never
+// returns an older value than an earlier one.
 __device__ __forceinline__ bool poll_batch(const MkParams& p, MkShared& sh, const u64* src, int total, int base,
                                            u64 (&wv)[MK_GATHER_MAXW], uint32_t epoch, int lane) {
   const u64* q = src + base + lane;
   const int lim = total - base - lane;      // word k is in range when 64k < lim
 #pragma unroll
-  for (int k = 0; k < MK_GATHER_MAXW; ++k) {
-    wv[k] = (u64)epoch << 32;
-    if (k * 64 < lim) wv[k] = ll_load(q + k * 64);
-  }
+  for (int k = 0; k < MK_GATHER_MAXW; ++k) wv[k] = ll_load(q + k * 64);
   Waiter wt(true);
   for (;;) {
-    bool bad = false;
+    int first_bad = -1;
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) bad |= !ll_ok(wv[k], epoch);
-    if (__ballot(bad) == 0) return true;
+    for (int k = MK_GATHER_MAXW - 1; k >= 0; --k)
+      first_bad = (k * 64 >= lim || ll_ok(wv[k], epoch)) ? first_bad : k;
+    if (__ballot(first_bad >= 0) == 0) return true;
     if (wt.tick(p, sh)) return false;
+    const u64 s = ll_load(q + (first_bad >= 0 ? first_bad * 64 : 0));
+    if (__ballot(first_bad >= 0 && ll_ok(s, epoch)) != 0) {
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k)
-      if (!ll_ok(wv[k], epoch)) wv[k] = ll_load(q + k * 64);
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) wv[k] = ll_load(q + k * 64);
+    }
   }
 }
 
@@ -677,6 +841,7 @@ __device__ __forceinline__ bool gather(const MkParams& p, MkShared& sh, const u6
   for (int base = 0; base < total; base += 64 * MK_GATHER_MAXW) {
     u64 wv[MK_GATHER_MAXW];
     if (!poll_batch(p, sh, src, total, base, wv, epoch, lane)) return false;
+    if (base + 64 * MK_GATHER_MAXW >= total) trace_mark(p, blockIdx.x, prev_done, 1, lane);
     if (!waited) {
       if (!wait_all_done(p, sh, prev_done)) return false;
       waited = true;
@@ -696,44 +861,84 @@ __device__ __forceinline__ bool gather(const MkParams& p, MkShared& sh, const u6
   return true;
 }
 
-// RMSNorm staging: act = x / sqrt(mean(x^2) + eps) * g, with x the residual stream
-// (the embedding row for the first layer).  Rows [res_r0, res_r0 + res_n) of the raw x
-// are kept for the residual add of the next O / DOWN instruction.
+// RMSNorm staging: act = x * (1 / sqrt(mean(x^2) + eps)) * g, with x the residual
+// stream (the embedding row for the first layer).  Rows [res_r0, res_r0 + res_n) of the
+// raw x are kept for the residual add of the next O / DOWN instruction.  The gains go
+// to LDS before any wait.  Vectors of up to 64 * MK_GATHER_MAXW values stay in
+// registers between the sum of squares and the scaled write (one LDS pass); longer ones
+// are normalised in place in a second pass.
 __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared& sh, const u64* src, const uint16_t* gain,
-                           int res_r0, int res_n, int i, uint32_t epoch, int lane) {
-  const int d = p.d;
-  const int npair = d >> 1;
-  uint32_t gw[MK_ACT_FLOATS / 128];                 // gain pairs, prefetched
+                                           int res_r0, int res_n, int i, uint32_t epoch, int lane) {
+  const int d = p.d, npair = d >> 1;
+  for (int b0 = 0; b0 < npair; b0 += 64 * 16) {   // gain pairs, 16 loads per lane per batch
+    uint32_t gp[16];
 #pragma unroll
-  for (int k = 0; k < MK_ACT_FLOATS / 128; ++k) {
-    const int q = k * 64 + lane;
-    gw[k] = q < npair ? ((const uint32_t*)gain)[q] : 0u;
+    for (int k = 0; k < 16; ++k) gp[k] = ((const uint32_t*)gain)[min(b0 + k * 64 + lane, npair - 1)];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pin(gp[k]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)   // lanes past the end rewrite the last pair with its own value
+      ((uint32_t*)sh.gain)[min(b0 + k * 64 + lane, npair - 1)] = gp[k];
+  }
+  if (d <= 64 * MK_GATHER_MAXW) {
+    float xv[MK_GATHER_MAXW];
+    if (src == nullptr) {
+      const uint16_t* e = p.embed + (size_t)sh.token * d;
+      uint32_t eb[MK_GATHER_MAXW];
+#pragma unroll
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) eb[k] = e[min(k * 64 + lane, d - 1)];
+#pragma unroll
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) pin(eb[k]);
+#pragma unroll
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) xv[k] = k * 64 + lane < d ? bf16f((uint16_t)eb[k]) : 0.f;
+    } else {
+      u64 wv[MK_GATHER_MAXW];
+      if (!poll_batch(p, sh, src, d, 0, wv, epoch, lane)) return false;
+      trace_mark(p, blockIdx.x, i, 1, lane);
+#pragma unroll
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) xv[k] = k * 64 + lane < d ? ll_val(wv[k]) : 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < MK_GATHER_MAXW; ++k) ss = fmaf(xv[k], xv[k], ss);
+    const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + p.eps);
+    if (!wait_all_done(p, sh, i)) return false;
+#pragma unroll
+    for (int k = 0; k < MK_GATHER_MAXW; ++k) {
+      const int idx = k * 64 + lane;
+      if (idx < d) {
+        sh.act[idx] = (xv[k] * rinv) * bf16f(sh.gain[idx]);
+        const int r = idx - res_r0;
+        if ((unsigned)r < (unsigned)res_n) sh.xres[r] = xv[k];
+      }
+    }
+    return true;
   }
   float ss = 0.f;
   if (src == nullptr) {
     const uint16_t* e = p.embed + (size_t)sh.token * d;
     if (!wait_all_done(p, sh, i)) return false;
-    for (int idx = lane; idx < d; idx += 64) {
-      const float v = bf16f(e[idx]);
-      sh.act[idx] = v;
-      ss = fmaf(v, v, ss);
+    for (int b0 = 0; b0 < d; b0 += 64 * 16) {
+      uint32_t eb[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) eb[k] = e[min(b0 + k * 64 + lane, d - 1)];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) pin(eb[k]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int idx = b0 + k * 64 + lane;
+        const float v = idx < d ? bf16f((uint16_t)eb[k]) : 0.f;
+        if (idx < d) sh.act[idx] = v;
+        ss = fmaf(v, v, ss);
+      }
     }
   } else {
     if (!gather(p, sh, src, d, sh.act, i, epoch, lane, &ss)) return false;
   }
-  ss = wave_sum(ss);
-  const float rms = sqrtf(ss / (float)d + p.eps);
+  const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + p.eps);
   lds_fence();
   for (int j = lane; j < res_n; j += 64) sh.xres[j] = sh.act[res_r0 + j];
-#pragma unroll
-  for (int k = 0; k < MK_ACT_FLOATS / 128; ++k) {
-    const int q = k * 64 + lane;
-    if (q < npair) {
-      const float a0 = sh.act[2 * q], a1 = sh.act[2 * q + 1];
-      sh.act[2 * q] = (a0 / rms) * bf_lo(gw[k]);
-      sh.act[2 * q + 1] = (a1 / rms) * bf_hi(gw[k]);
-    }
-  }
+  for (int idx = lane; idx < d; idx += 64) sh.act[idx] = (sh.act[idx] * rinv) * bf16f(sh.gain[idx]);
   return true;
 }
 
@@ -752,11 +957,13 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared& sh, cons
   const u64* src = p.ll_qkv + (size_t)l * p.nqkv + (size_t)gi * total;   // group-major q | k | v
   if (!gather(p, sh, src, total, sh.act, i, epoch, lane, nullptr)) return false;
   lds_fence();
-  const float* cs = p.rope + (size_t)g.pos * hd;   // [half][2]
+  // cos / sin of the lane's rotation pair: t = lane + 64j has t % half == lane % half
+  // because half (32 or 64) divides 64, so one pair per lane serves every t.
+  const float* cs = p.rope + (size_t)g.pos * hd + 2 * (lane & (half - 1));   // [half][2]
+  const float c = cs[0], sn = cs[1];
   for (int t = lane; t < (hpg + 1) * half; t += 64) {
     const int hh = t / half, e = t - hh * half;
     float* v = sh.act + hh * hd;
-    const float c = cs[2 * e], sn = cs[2 * e + 1];
     const float a = v[e], b = v[e + half];
     v[e] = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, sn));
     v[e + half] = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, sn));
@@ -865,9 +1072,14 @@ __device__ __forceinline__ void lm_finalize(const MkParams& p, MkShared& sh, uin
   old = __shfl(old, 0);
   if (old != (uint32_t)(p.n_cus - 1)) return;
   u64 best = 0;
-  for (int c = lane; c < p.n_cus; c += 64) {
-    const u64 k = __hip_atomic_load(p.amax + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    best = k > best ? k : best;
+  for (int c0 = 0; c0 < p.n_cus; c0 += 256) {
+    u64 k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      k[j] = __hip_atomic_load(p.amax + min(c0 + 64 * j + lane, p.n_cus - 1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) best = k[j] > best ? k[j] : best;   // a repeated key changes nothing
   }
   best = wave_max_u64(best);
   if (lane == 0) {
@@ -883,6 +1095,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared& sh, cin
     const MkInstr in = list[i];
     const int l = in.layer;
     lane = opaque(lane);
+    trace_mark(p, cu, i, 0, lane);
     bool ok = true;
     switch (in.op) {
       case MK_OP_QKV:
@@ -910,6 +1123,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared& sh, cin
     if (!ok) return;
     lds_fence();
     if (lane == 0) lds_store(&sh.act_seq, i + 1);
+    trace_mark(p, cu, i, 2, lane);
     if (in.op == MK_OP_ATTN) {
       if (!wait_all_done(p, sh, i + 1)) return;
       if (!attn_finalize(p, sh, in, g, i, epoch, lane)) return;
@@ -917,6 +1131,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared& sh, cin
       if (!wait_all_done(p, sh, i + 1)) return;
       lm_finalize(p, sh, epoch, cu, lane);
     }
+    trace_mark(p, cu, i, 3, lane);
   }
 }
 
@@ -935,6 +1150,10 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
       sh.done[w] = 0;
       sh.amax[w] = 0;
     }
+    for (int k = 0; k < MK_MAX_SLOTS; ++k) {
+      sh.full[k] = 0;
+      sh.freed[k] = 0;
+    }
     sh.epoch = __hip_atomic_load(&p.ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int t = p.token_dev ? p.token_dev[0] : p.token;
     if (t < 0 || t >= p.V) {
@@ -950,5 +1169,6 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   cinstr_t list = (cinstr_t)p.plan + o0;
   const StepGeo g = step_geo(p, p.pos);
   if (wave < MK_NC) compute_wave(p, sh, list, nins, g, wave, lane, epoch);
+  else if (wave < MK_NC + MK_NL) loader_wave(p, sh, list, nins, g, wave - MK_NC, lane);
   else leader_wave(p, sh, list, nins, g, lane, epoch, cu);
 }

@@ -98,7 +98,7 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
   MkPlan p;
   p.n_cus = n_cus;
   p.page_bytes = pick_page_bytes(c, nch);
-  p.npw = MK_PAGES_BYTES / (MK_NC * p.page_bytes);
+  p.slots = MK_PAGES_BYTES / p.page_bytes;
   if (2 * c.hidden * 2 > p.page_bytes || p.page_bytes / (4 * c.hidden) > MK_GATE_SCRATCH) {
     if (why) *why = "gate/up page geometry unsupported";
     return MK_EINVAL;

@@ -9,7 +9,7 @@
 struct MkPlan {
   int n_cus = 0;
   int page_bytes = 0;   // bytes per LDS page
-  int npw = 0;          // pages per compute wave
+  int slots = 0;        // pages in the LDS ring
   int s_max = 0;        // attention splits per KV head
   int min_chunk = 0;    // fewest keys one split covers
   std::vector<int32_t> off;      // [n_cus + 1] list offsets into rec

@@ -7,21 +7,26 @@
 #pragma once
 #include <stdint.h>
 
-// Work-group shape: MK_NC compute waves that stream weights through private LDS
-// page rings, plus one leader wave that waits on dependencies and stages the
-// activation vector.  One work-group per CU.
+// Work-group shape, one work-group per CU: MK_NC compute waves that only read LDS,
+// MK_NL loader waves that only stream pages HBM -> LDS, and one leader wave that
+// waits on dependencies and stages the activation vector.
 #define MK_NC 4
-#define MK_NWAVES (MK_NC + 1)
+#define MK_NL 2
+#define MK_NWAVES (MK_NC + MK_NL + 1)
 #define MK_THREADS (64 * MK_NWAVES)
+#define MK_MAX_SLOTS 32
 
 // LDS budget (gfx950 has 160 KiB per work-group).
 #define MK_ACT_FLOATS 4096                // activation vector staged per instruction
-#define MK_PAGES_BYTES (128 * 1024)       // page pool, split evenly between compute waves
+#define MK_PAGES_BYTES (128 * 1024)       // page ring shared by the loaders and compute waves
 #define MK_MAX_RES_ROWS 64                // rows of x one CU owns in a residual op
 #define MK_GATE_SCRATCH 16                // gate results held per wave until the up row
 #define MK_MAX_HPG 8                      // query heads per KV head
 #define MK_PART_OFF 1024                  // offset (floats) of per-wave attention partials in act
 #define MK_GATHER_MAXW 32                 // words per lane one gather batch holds
+// The activation-word arena is padded by one gather batch, so a batch may load past the
+// end of the vector it polls without a bounds test per word.
+#define MK_LL_PAD (64 * MK_GATHER_MAXW)
 
 // Instruction opcodes — the article's six fused instructions.
 enum {
@@ -65,7 +70,7 @@ struct MkParams {
   int32_t nq, nkv, nqkv, hpg;
   float eps, attn_scale;
   // schedule
-  int32_t n_cus, page_bytes, npw, lpp, s_max, min_chunk;
+  int32_t n_cus, page_bytes, nslot, lpp, s_max, min_chunk;   // nslot: pages in the LDS ring
   // weights (bf16)
   const uint16_t* embed;
   const uint16_t* lm_head;
@@ -90,4 +95,11 @@ struct MkParams {
   const int32_t* token_dev;       // [1] or null
   int32_t token, pos;
   long long watchdog_ticks;       // s_memrealtime ticks (100 MHz)
+  // optional timestamp trace [n_cus][trace_len][MK_TRACE_SLOTS] (s_memrealtime ticks)
+  unsigned long long* trace;
+  int32_t trace_len;
 };
+
+// Trace slots per instruction: leader start, inputs ready, activation staged, leader
+// done (after attention merge / argmax), then the finish time of each compute wave.
+#define MK_TRACE_SLOTS 8

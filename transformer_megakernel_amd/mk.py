@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.mk_plan_info.argtypes = [vp, ctypes.POINTER(i32)]
         L.mk_plan_copy.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), i64]
         L.mk_debug_dump.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), i64, ctypes.POINTER(i64)]
+        L.mk_set_trace.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
         L.mk_destroy.argtypes = [vp]
         L.mk_destroy.restype = None
         L.mk_strerror.argtypes = [ctypes.c_int]
@@ -167,7 +168,22 @@ class Megakernel:
         _check(lib().mk_plan_copy(self._h, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                   rec.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), rec.size), "mk_plan_copy")
         return dict(n_cus=n_cus, offsets=off, records=rec.reshape(n_rec, words), page_bytes=info[3],
-                    pages_per_wave=info[4], compute_waves=info[5], s_max=info[6], lds_bytes=info[7])
+                    ring_pages=info[4], compute_waves=info[5], s_max=info[6], lds_bytes=info[7])
+
+    def enable_trace(self, device="cuda:0"):
+        """Allocate a trace buffer (torch, on the device) and start recording; returns it."""
+        import torch
+        need = ctypes.c_int64()
+        _check(lib().mk_set_trace(self._h, None, 0, ctypes.byref(need)), "mk_set_trace")
+        buf = torch.zeros(need.value, dtype=torch.int64, device=device)
+        _check(lib().mk_set_trace(self._h, _ptr(buf), need.value, ctypes.byref(need)), "mk_set_trace")
+        self._trace = buf
+        return buf
+
+    def disable_trace(self):
+        need = ctypes.c_int64()
+        _check(lib().mk_set_trace(self._h, None, 0, ctypes.byref(need)), "mk_set_trace")
+        self._trace = None
 
     def debug_dump(self) -> dict:
         """Intermediates of the last step as (values fp32, epochs) per buffer."""
