@@ -10,7 +10,6 @@ Prints one JSON line (rank 0).  Other workloads (--workload) are for the design 
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,20 +28,13 @@ WORKLOADS = {
 METRIC = "batch-1 decode steps/sec (Llama-3.2-1B shape); achieved HBM GB/s vs peak"
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "transformer_megakernel_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def stored_traffic(workload: str, n_launch_bytes: float):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they were taken on
     the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
+    from transformer_megakernel_amd.profile_summary import kernel_source_hash
     t = json.load(open(path))
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
@@ -68,6 +60,20 @@ def cpu_baseline(shape, W, kv, tok, pos, budget_s=20.0):
                 sample=f"{n} decode steps of the same workload (NumPy fp32 oracle, {el:.1f} s)")
 
 
+def copy_calibration(mib: int) -> None:
+    """Three elementwise copies (dst = -src, int32) of ``mib`` MiB: per dispatch the HBM
+    counters should read ``mib`` MiB fetched and ``mib`` MiB written."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,7 +81,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama1b_ctx128", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (a plain copy kernel of known "
+                         "size, to calibrate the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
               "the decode megakernel has no multi-GPU path", file=sys.stderr)

@@ -800,8 +800,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared& sh, ci
 // before the next (a full round trip per load).  Out-of-range lanes load a valid
 // address and discard the value.
 
-// Poll words [base, base + 64*MK_GATHER_MAXW) of src until all carry this step's
-// epoch.  Word base + 64k + lane lands in wv[k]; words past `total` are loaded (the
+// Poll words [base, base + 64*NW) of src until all carry this step's epoch.  Word base + 64k + lane lands in wv[k]; words past `total` are loaded (the
 // arena is padded by MK_LL_PAD words) but not waited for.
 // The first pass loads every word; while words are missing, each lane re-polls only its
 // first missing word (one load per lane per round trip) and the wave reloads the whole
@@ -809,24 +808,28 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared& sh, ci
 // the weight stream for HBM.  Reloading a word that already carries the epoch is
 // harmless: each word is written once per step, and a later load of a location never
 // returns an older value than an earlier one.
+template <int NW = MK_GATHER_MAXW>
 __device__ __forceinline__ bool poll_batch(const MkParams& p, MkShared& sh, const u64* src, int total, int base,
-                                           u64 (&wv)[MK_GATHER_MAXW], uint32_t epoch, int lane) {
+                                           u64 (&wv)[NW], uint32_t epoch, int lane) {
   const u64* q = src + base + lane;
   const int lim = total - base - lane;      // word k is in range when 64k < lim
 #pragma unroll
-  for (int k = 0; k < MK_GATHER_MAXW; ++k) wv[k] = ll_load(q + k * 64);
+  for (int k = 0; k < NW; ++k) wv[k] = ll_load(q + k * 64);
   Waiter wt(true);
   for (;;) {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) all = all && (ll_ok(wv[k], epoch) || k * 64 >= lim);
+    if (__ballot(!all) == 0) return true;
     int first_bad = -1;
 #pragma unroll
-    for (int k = MK_GATHER_MAXW - 1; k >= 0; --k)
+    for (int k = NW - 1; k >= 0; --k)
       first_bad = (k * 64 >= lim || ll_ok(wv[k], epoch)) ? first_bad : k;
-    if (__ballot(first_bad >= 0) == 0) return true;
     if (wt.tick(p, sh)) return false;
     const u64 s = ll_load(q + (first_bad >= 0 ? first_bad * 64 : 0));
     if (__ballot(first_bad >= 0 && ll_ok(s, epoch)) != 0) {
 #pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) wv[k] = ll_load(q + k * 64);
+      for (int k = 0; k < NW; ++k) wv[k] = ll_load(q + k * 64);
     }
   }
 }
@@ -846,13 +849,22 @@ __device__ __forceinline__ bool gather(const MkParams& p, MkShared& sh, const u6
       if (!wait_all_done(p, sh, prev_done)) return false;
       waited = true;
     }
+    if (total - base >= 64 * MK_GATHER_MAXW) {   // a full batch: no per-word test
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) {
-      const int idx = base + k * 64 + lane;
-      if (idx < total) {
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) {
         const float v = ll_val(wv[k]);
-        dst[idx] = v;
+        dst[base + k * 64 + lane] = v;
         acc = fmaf(v, v, acc);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) {
+        const int idx = base + k * 64 + lane;
+        if (idx < total) {
+          const float v = ll_val(wv[k]);
+          dst[idx] = v;
+          acc = fmaf(v, v, acc);
+        }
       }
     }
   }
@@ -881,6 +893,7 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared& sh, cons
       ((uint32_t*)sh.gain)[min(b0 + k * 64 + lane, npair - 1)] = gp[k];
   }
   if (d <= 64 * MK_GATHER_MAXW) {
+    const int kmax = d >> 6;   // hidden is a multiple of 64: word k is in range iff k < kmax
     float xv[MK_GATHER_MAXW];
     if (src == nullptr) {
       const uint16_t* e = p.embed + (size_t)sh.token * d;
@@ -896,22 +909,37 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared& sh, cons
       if (!poll_batch(p, sh, src, d, 0, wv, epoch, lane)) return false;
       trace_mark(p, blockIdx.x, i, 1, lane);
 #pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) xv[k] = k * 64 + lane < d ? ll_val(wv[k]) : 0.f;
+      for (int k = 0; k < MK_GATHER_MAXW; ++k) xv[k] = k < kmax ? ll_val(wv[k]) : 0.f;
     }
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < MK_GATHER_MAXW; ++k) ss = fmaf(xv[k], xv[k], ss);
     const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + p.eps);
-    if (!wait_all_done(p, sh, i)) return false;
+    // All LDS reads first, then all writes: a read issued after a write waits for it.
+    uint32_t gl[MK_GATHER_MAXW];
+#pragma unroll
+    for (int k = 0; k < MK_GATHER_MAXW; ++k) gl[k] = sh.gain[(k < kmax ? k * 64 : 0) + lane];
+#pragma unroll
+    for (int k = 0; k < MK_GATHER_MAXW; ++k) pin(gl[k]);
+    float nv[MK_GATHER_MAXW];
+#pragma unroll
+    for (int k = 0; k < MK_GATHER_MAXW; ++k) nv[k] = (xv[k] * rinv) * bf16f((uint16_t)gl[k]);
+    // Residual rows res_r0 + j (j < res_n <= 64) lie in words k0 and k0 + 1: pick those two
+    // words with uniform selects, then fetch each row's value from the lane that holds it.
+    const int k0 = res_r0 >> 6;
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int k = 0; k < MK_GATHER_MAXW; ++k) {
-      const int idx = k * 64 + lane;
-      if (idx < d) {
-        sh.act[idx] = (xv[k] * rinv) * bf16f(sh.gain[idx]);
-        const int r = idx - res_r0;
-        if ((unsigned)r < (unsigned)res_n) sh.xres[r] = xv[k];
-      }
+      a0 = k == k0 ? xv[k] : a0;
+      a1 = k == k0 + 1 ? xv[k] : a1;
     }
+    const int ridx = res_r0 + lane;
+    const float b0 = __shfl(a0, ridx & 63), b1 = __shfl(a1, ridx & 63);
+    if (!wait_all_done(p, sh, i)) return false;
+#pragma unroll
+    for (int k = 0; k < MK_GATHER_MAXW; ++k)
+      if (k < kmax) sh.act[k * 64 + lane] = nv[k];
+    if (lane < res_n) sh.xres[lane] = (ridx >> 6) == k0 ? b0 : b1;
     return true;
   }
   float ss = 0.f;
@@ -949,39 +977,53 @@ __device__ __forceinline__ bool stage_raw(const MkParams& p, MkShared& sh, const
 
 // Attention staging for item (kv head g, split s): q of the group's heads, the new k
 // and v; RoPE on q and k; k, v rounded to bf16 (what the cache holds).  The split that
-// contains the current position writes k, v into cache slot pos.
-__device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared& sh, const MkInstr& in, const StepGeo& g, int i,
-                           uint32_t epoch, int lane) {
+// contains the current position writes k, v into cache slot pos.  Everything happens in
+// registers between the poll and one batch of LDS writes.  Word idx = 64j + lane of the
+// group holds element e = idx % hd of head idx / hd; its rotation partner e +- hd/2 is
+// in lane ^ 32 of the same word (hd 64) or in the same lane of word j ^ 1 (hd 128).
+constexpr int MK_ATTN_NW = 12;   // (4 + 2) heads x 128 / 64: words per lane of the largest group
+__device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared& sh, const MkInstr& in, const StepGeo& g,
+                                           int i, uint32_t epoch, int lane) {
   const int hd = p.hd, hpg = p.hpg, half = hd >> 1, l = in.layer, gi = in.a;
   const int total = (hpg + 2) * hd;
   const u64* src = p.ll_qkv + (size_t)l * p.nqkv + (size_t)gi * total;   // group-major q | k | v
-  if (!gather(p, sh, src, total, sh.act, i, epoch, lane, nullptr)) return false;
-  lds_fence();
-  // cos / sin of the lane's rotation pair: t = lane + 64j has t % half == lane % half
-  // because half (32 or 64) divides 64, so one pair per lane serves every t.
-  const float* cs = p.rope + (size_t)g.pos * hd + 2 * (lane & (half - 1));   // [half][2]
+  const float* cs = p.rope + (size_t)g.pos * hd + 2 * (lane & (half - 1));  // [half][2], e % half == lane % half
   const float c = cs[0], sn = cs[1];
-  for (int t = lane; t < (hpg + 1) * half; t += 64) {
-    const int hh = t / half, e = t - hh * half;
-    float* v = sh.act + hh * hd;
-    const float a = v[e], b = v[e + half];
-    v[e] = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, sn));
-    v[e + half] = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, sn));
+  u64 wv[MK_ATTN_NW];
+  if (!poll_batch<MK_ATTN_NW>(p, sh, src, total, 0, wv, epoch, lane)) return false;
+  trace_mark(p, blockIdx.x, i, 1, lane);
+  float v[MK_ATTN_NW];
+#pragma unroll
+  for (int j = 0; j < MK_ATTN_NW; ++j) v[j] = ll_val(wv[j]);
+  float pr[MK_ATTN_NW];   // rotation partners
+  const bool hd64 = hd == 64;
+#pragma unroll
+  for (int j = 0; j < MK_ATTN_NW; ++j) {
+    const float x = __shfl_xor(v[j], 32);
+    pr[j] = hd64 ? x : v[j ^ 1];
   }
-  lds_fence();
+  const int kbase = hpg * hd, vbase = (hpg + 1) * hd;   // offsets of k and v in the group
   const bool has_pos = in.b == g.s_eff - 1;
   uint16_t* kslot = p.kv + ((((size_t)l * 2) * p.hkv + gi) * p.max_ctx + g.pos) * hd;
   uint16_t* vslot = kslot + (size_t)p.hkv * p.max_ctx * hd;
-  for (int e = lane; e < hd; e += 64) {
-    const uint16_t kb = f2bf(sh.act[hpg * hd + e]);
-    const uint16_t vb = f2bf(sh.act[(hpg + 1) * hd + e]);
-    sh.act[hpg * hd + e] = bf16f(kb);
-    sh.act[(hpg + 1) * hd + e] = bf16f(vb);
-    if (has_pos) {
-      kslot[e] = kb;
-      vslot[e] = vb;
+#pragma unroll
+  for (int j = 0; j < MK_ATTN_NW; ++j) {
+    const int idx = j * 64 + lane;
+    const bool first = hd64 ? lane < 32 : (j & 1) == 0;   // e < half
+    if (idx < vbase) {   // q heads and k: rotate
+      v[j] = first ? __fsub_rn(__fmul_rn(v[j], c), __fmul_rn(pr[j], sn))
+                   : __fadd_rn(__fmul_rn(v[j], c), __fmul_rn(pr[j], sn));
+    }
+    if (idx >= kbase && idx < total) {   // k and v: what the cache holds
+      const uint16_t b = f2bf(v[j]);
+      v[j] = bf16f(b);
+      if (has_pos) (idx < vbase ? kslot : vslot)[idx - (idx < vbase ? kbase : vbase)] = b;
     }
   }
+  if (!wait_all_done(p, sh, i)) return false;
+#pragma unroll
+  for (int j = 0; j < MK_ATTN_NW; ++j)
+    if (j * 64 + lane < total) sh.act[j * 64 + lane] = v[j];
   return true;
 }
 
@@ -991,38 +1033,64 @@ __device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, in
 
 // After the compute waves: combine their partials (and the current position's key)
 // into this split's (m, l, o), then either write o (single split), publish the split,
-// and/or merge all splits of one head (CUs with split index < heads per group).
-__device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared& sh, const MkInstr& in, const StepGeo& g, int i,
-                              uint32_t epoch, int lane) {
-  const int hd = p.hd, hpg = p.hpg, l = in.layer, gi = in.a, s = in.b;
-  const int stride = hd + 2;
+// and/or merge all splits of one head (CUs with split index < heads per group).  Lane
+// `lane` handles elements lane + 64c of each head.  LDS reads are batched ahead of use.
+template <int HD, int HPG>
+__device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared& sh, const MkInstr& in, const StepGeo& g,
+                                              int i, uint32_t epoch, int lane) {
+  constexpr int E = HD / 64, STRIDE = HD + 2;
+  const int l = in.layer, gi = in.a, s = in.b;
   if (s < g.s_eff) {
     const bool has_pos = s == g.s_eff - 1;
-    for (int h = 0; h < hpg; ++h) {
-      float M = -INFINITY;
-      for (int w = 0; w < MK_NC; ++w) M = fmaxf(M, sh.act[MK_PART_OFF + (w * hpg + h) * stride]);
-      float sp = -INFINITY;
-      if (has_pos) {
-        float acc = 0.f;
-        for (int e = lane; e < hd; e += 64) acc = fmaf(sh.act[h * hd + e], sh.act[hpg * hd + e], acc);
-        sp = wave_sum(acc) * p.attn_scale;
-        M = fmaxf(M, sp);
+    const float* part = sh.act + MK_PART_OFF;
+    float mw[MK_NC][HPG], lw[MK_NC][HPG], ow[MK_NC][HPG][E], qv[HPG][E], kn[E], vn[E];
+#pragma unroll
+    for (int w = 0; w < MK_NC; ++w)
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) {
+        mw[w][h] = part[(w * HPG + h) * STRIDE];
+        lw[w][h] = part[(w * HPG + h) * STRIDE + 1];
+#pragma unroll
+        for (int c = 0; c < E; ++c) ow[w][h][c] = part[(w * HPG + h) * STRIDE + 2 + c * 64 + lane];
       }
-      float L = 0.f;
-      float wgt[MK_NC];
+#pragma unroll
+    for (int c = 0; c < E; ++c) {
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) qv[h][c] = sh.act[h * HD + c * 64 + lane];
+      kn[c] = sh.act[HPG * HD + c * 64 + lane];
+      vn[c] = sh.act[(HPG + 1) * HD + c * 64 + lane];
+    }
+    float sp[HPG];   // score of the current position (the key that is not in the cache yet)
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < E; ++c) acc = fmaf(qv[h][c], kn[c], acc);
+      sp[h] = acc;
+    }
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) sp[h] = has_pos ? wave_sum(sp[h]) * p.attn_scale : -INFINITY;
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      float M = sp[h];
+#pragma unroll
+      for (int w = 0; w < MK_NC; ++w) M = fmaxf(M, mw[w][h]);
+      float L = 0.f, wt[MK_NC];
+#pragma unroll
       for (int w = 0; w < MK_NC; ++w) {
-        const float mw = sh.act[MK_PART_OFF + (w * hpg + h) * stride];
-        wgt[w] = mw == -INFINITY ? 0.f : __expf(mw - M);
-        L = fmaf(sh.act[MK_PART_OFF + (w * hpg + h) * stride + 1], wgt[w], L);
+        wt[w] = mw[w][h] == -INFINITY ? 0.f : __expf(mw[w][h] - M);
+        L = fmaf(lw[w][h], wt[w], L);
       }
-      const float wp = has_pos ? __expf(sp - M) : 0.f;
+      const float wp = has_pos ? __expf(sp[h] - M) : 0.f;
       L += wp;
-      for (int e = lane; e < hd; e += 64) {
-        float o = 0.f;
-        for (int w = 0; w < MK_NC; ++w) o = fmaf(sh.act[MK_PART_OFF + (w * hpg + h) * stride + 2 + e], wgt[w], o);
-        if (has_pos) o = fmaf(wp, sh.act[(hpg + 1) * hd + e], o);
+#pragma unroll
+      for (int c = 0; c < E; ++c) {
+        float o = wp * vn[c];
+#pragma unroll
+        for (int w = 0; w < MK_NC; ++w) o = fmaf(ow[w][h][c], wt[w], o);
+        const int e = c * 64 + lane;
         if (g.s_eff == 1)
-          ll_store(p.ll_o + (size_t)l * p.nq + (gi * hpg + h) * hd + e, o / L, epoch);
+          ll_store(p.ll_o + (size_t)l * p.nq + (gi * HPG + h) * HD + e, o / L, epoch);
         else
           ll_store(p.ll_part + part_index(p, l, gi, h, s) + 2 + e, o, epoch);
       }
@@ -1032,29 +1100,29 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared& sh, c
       }
     }
   }
-  if (g.s_eff > 1 && s < hpg) {
+  if (g.s_eff > 1 && s < HPG) {
     // Merge head s of this group over all splits.
     const int h = s;
     lds_fence();
-    if (!gather(p, sh, p.ll_part + part_index(p, l, gi, h, 0), g.s_eff * stride, sh.act, i + 1, epoch, lane,
+    if (!gather(p, sh, p.ll_part + part_index(p, l, gi, h, 0), g.s_eff * STRIDE, sh.act, i + 1, epoch, lane,
                 nullptr))
       return false;
     lds_fence();
     float M = -INFINITY;
-    for (int t = 0; t < g.s_eff; ++t) M = fmaxf(M, sh.act[t * stride]);
-    float L = 0.f;
+    for (int t = 0; t < g.s_eff; ++t) M = fmaxf(M, sh.act[t * STRIDE]);
+    float L = 0.f, o[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) o[c] = 0.f;
     for (int t = 0; t < g.s_eff; ++t) {
-      const float mt = sh.act[t * stride];
-      if (mt != -INFINITY) L = fmaf(sh.act[t * stride + 1], __expf(mt - M), L);
+      const float mt = sh.act[t * STRIDE];
+      const float wt = mt == -INFINITY ? 0.f : __expf(mt - M);
+      L = fmaf(sh.act[t * STRIDE + 1], wt, L);
+#pragma unroll
+      for (int c = 0; c < E; ++c) o[c] = fmaf(sh.act[t * STRIDE + 2 + c * 64 + lane], wt, o[c]);
     }
-    for (int e = lane; e < hd; e += 64) {
-      float o = 0.f;
-      for (int t = 0; t < g.s_eff; ++t) {
-        const float mt = sh.act[t * stride];
-        if (mt != -INFINITY) o = fmaf(sh.act[t * stride + 2 + e], __expf(mt - M), o);
-      }
-      ll_store(p.ll_o + (size_t)l * p.nq + (gi * hpg + h) * hd + e, o / L, epoch);
-    }
+#pragma unroll
+    for (int c = 0; c < E; ++c)
+      ll_store(p.ll_o + (size_t)l * p.nq + (gi * HPG + h) * HD + c * 64 + lane, o[c] / L, epoch);
   }
   return true;
 }
@@ -1126,7 +1194,17 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared& sh, cin
     trace_mark(p, cu, i, 2, lane);
     if (in.op == MK_OP_ATTN) {
       if (!wait_all_done(p, sh, i + 1)) return;
-      if (!attn_finalize(p, sh, in, g, i, epoch, lane)) return;
+      bool fin;
+      if (p.hd == 64) {
+        fin = p.hpg == 4 ? attn_finalize<64, 4>(p, sh, in, g, i, epoch, lane)
+            : p.hpg == 2 ? attn_finalize<64, 2>(p, sh, in, g, i, epoch, lane)
+                         : attn_finalize<64, 1>(p, sh, in, g, i, epoch, lane);
+      } else {
+        fin = p.hpg == 4 ? attn_finalize<128, 4>(p, sh, in, g, i, epoch, lane)
+            : p.hpg == 2 ? attn_finalize<128, 2>(p, sh, in, g, i, epoch, lane)
+                         : attn_finalize<128, 1>(p, sh, in, g, i, epoch, lane);
+      }
+      if (!fin) return;
     } else if (in.op == MK_OP_LMHEAD) {
       if (!wait_all_done(p, sh, i + 1)) return;
       lm_finalize(p, sh, epoch, cu, lane);
