@@ -3,6 +3,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <algorithm>
 #include <cstring>
 #include <string>
@@ -11,6 +12,7 @@
 #include "../../include/mk.h"
 #include "mk_kernel.h"
 #include "mk_plan.h"
+#include "mk_shapes.h"
 
 struct mk_ctx {
   mk_config cfg{};
@@ -21,6 +23,7 @@ struct mk_ctx {
   bool needs_reset = false;
   long long watchdog_us = 2000000;
   MkPlan plan;
+  const void* kernel = nullptr;   // the step kernel compiled for this shape
   // borrowed weights
   const uint16_t* embed = nullptr;
   const uint16_t* lm_head = nullptr;
@@ -42,7 +45,29 @@ struct mk_ctx {
 
 namespace {
 
-thread_local char g_hip_msg[256] = "";
+thread_local char g_hip_msg[512] = "";
+
+// One step-kernel instance per compiled shape, with its LDS ring size.
+struct ShapeKernel {
+  int D, HQ, HKV, HD, F;
+  const void* kernel;
+  int nslot;       // pages in the LDS ring
+  int lds_bytes;   // LDS of one work-group
+};
+#define MK_KERNEL_ENTRY(D, HQ, HKV, HD, F, NCH)                                                    \
+  {D, HQ, HKV, HD, F, (const void*)mk_step_kernel<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>,          \
+   mkdev::Ring<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>::NSLOT,                                     \
+   (int)sizeof(mkdev::MkShared<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>) +                          \
+       mkdev::Ring<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>::NSLOT * MK_PAGE_BYTES},
+const ShapeKernel kShapeKernels[] = {MK_SHAPES(MK_KERNEL_ENTRY)};
+#undef MK_KERNEL_ENTRY
+
+const ShapeKernel* shape_kernel(const mk_config& c) {
+  for (const ShapeKernel& k : kShapeKernels)
+    if (k.D == c.hidden && k.HQ == c.n_q_heads && k.HKV == c.n_kv_heads && k.HD == c.head_dim && k.F == c.ffn)
+      return &k;
+  return nullptr;
+}
 
 int hip_fail(hipError_t e, const char* what) {
   snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s", what, hipGetErrorString(e));
@@ -72,7 +97,7 @@ void free_device(mk_ctx* c) {
 }
 
 int reset_device_state(mk_ctx* c, hipStream_t s) {
-  HIPCHK(hipMemsetAsync(c->d_ll, 0, (c->ll_words + MK_LL_PAD) * sizeof(unsigned long long), s));
+  HIPCHK(hipMemsetAsync(c->d_ll, 0, c->ll_words * sizeof(unsigned long long), s));
   MkCtrl ctrl{};
   ctrl.epoch = 1;
   HIPCHK(hipMemcpyAsync(c->d_ctrl, &ctrl, sizeof(ctrl), hipMemcpyHostToDevice, s));
@@ -96,28 +121,16 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   const mk_config& g = c->cfg;
   MkParams p{};
   p.n_layers = g.n_layers;
-  p.d = g.hidden;
-  p.hq = g.n_q_heads;
-  p.hkv = g.n_kv_heads;
-  p.hd = g.head_dim;
-  p.F = g.ffn;
   p.V = g.vocab;
   p.max_ctx = g.max_ctx;
-  p.nq = g.n_q_heads * g.head_dim;
-  p.nkv = g.n_kv_heads * g.head_dim;
-  p.nqkv = p.nq + 2 * p.nkv;
-  p.hpg = g.n_q_heads / g.n_kv_heads;
-  p.eps = g.rms_eps;
-  p.attn_scale = (float)(1.0 / std::sqrt((double)g.head_dim));
   p.n_cus = c->plan.n_cus;
-  p.page_bytes = c->plan.page_bytes;
   p.nslot = c->plan.slots;
-  p.lpp = c->plan.page_bytes / 1024;
   p.s_max = c->plan.s_max;
   p.min_chunk = c->plan.min_chunk;
+  p.eps = g.rms_eps;
+  p.attn_scale = (float)(1.0 / std::sqrt((double)g.head_dim));
   p.embed = c->embed;
   p.lm_head = c->lm_head;
-  p.final_norm = c->final_norm;
   p.layers = c->d_layers;
   p.rope = c->d_rope;
   p.plan_off = c->d_off;
@@ -139,8 +152,7 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   p.trace = c->trace;
   p.trace_len = c->trace_len;
   void* args[] = {&p};
-  HIPCHK(hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(c->plan.n_cus), dim3(MK_THREADS), args, 0,
-                                    s));
+  HIPCHK(hipLaunchCooperativeKernel(c->kernel, dim3(c->plan.n_cus), dim3(MK_THREADS), args, 0, s));
   return MK_OK;
 }
 
@@ -171,6 +183,7 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
   c->cfg = *cfg;
   c->device = hip_device;
   c->n_cus = prop.multiProcessorCount;
+  c->kernel = shape_kernel(*cfg)->kernel;
   *out = c;
   return MK_OK;
 }
@@ -189,6 +202,7 @@ int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out) {
     delete c;
     return rc;
   }
+  c->plan.slots = shape_kernel(*cfg)->nslot;
   *out = c;
   return MK_OK;
 }
@@ -231,6 +245,7 @@ int mk_load_weights(mk_ctx* c, const mk_weights* w) {
     snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", why.c_str());
     return rc;
   }
+  plan.slots = shape_kernel(g)->nslot;
   HIPCHK(hipSetDevice(c->device));
   free_device(c);
   c->plan = std::move(plan);
@@ -270,7 +285,7 @@ int mk_load_weights(mk_ctx* c, const mk_weights* w) {
       (rc = alloc((void**)&c->d_off, c->plan.off.size() * sizeof(int32_t))) ||
       (rc = alloc((void**)&c->d_plan, c->plan.rec.size() * sizeof(MkInstr))) ||
       (rc = alloc((void**)&c->d_rope, rope.size() * sizeof(float))) ||
-      (rc = alloc((void**)&c->d_ll, (c->ll_words + MK_LL_PAD) * sizeof(unsigned long long))) ||
+      (rc = alloc((void**)&c->d_ll, c->ll_words * sizeof(unsigned long long))) ||
       (rc = alloc((void**)&c->d_amax, c->plan.n_cus * sizeof(unsigned long long))) ||
       (rc = alloc((void**)&c->d_ctrl, sizeof(MkCtrl))) || (rc = alloc((void**)&c->d_next, 64))) {
     free_device(c);
@@ -333,7 +348,7 @@ int mk_plan_info(const mk_ctx* c, int32_t info[8]) {
   info[4] = c->plan.slots;
   info[5] = MK_NC;
   info[6] = c->plan.s_max;
-  info[7] = (int32_t)sizeof(mkdev::MkShared);
+  info[7] = shape_kernel(c->cfg)->lds_bytes;
   return MK_OK;
 }
 

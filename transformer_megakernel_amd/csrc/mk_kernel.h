@@ -8,26 +8,27 @@
 //  * Paged LDS with early weight loads.  The article pages shared memory so that the
 //    next instruction's weights load while the current one computes.  Here MK_NL
 //    loader waves stream every page of the CU's list into one LDS ring with
-//    global_load_lds_dwordx4 (HBM -> LDS, no registers), across instruction
-//    boundaries and before the data an instruction depends on exists: weights and
-//    cached keys never depend on this step's activations.  A loader knows a page is
-//    complete from its own vmcnt and raises the slot's LDS flag; compute waves never
-//    issue loads, so a wait for data never stalls behind the weight stream.  The
-//    compiler is kept out of the DMA accounting (it would otherwise wait for every
-//    load before any LDS access).
+//    global_load_lds_dwordx4 (HBM -> LDS, no registers, non-temporal), across
+//    instruction boundaries and before the data an instruction depends on exists:
+//    weights and cached keys never depend on this step's activations.  A loader
+//    knows a page is complete from its own vmcnt and raises the slot's LDS flag;
+//    compute waves never issue loads, so a wait for data never stalls behind the
+//    weight stream.
 //  * Dependencies without grid barriers.  The article uses integer counters in
 //    global memory; on gfx950 the eight XCDs have separate L2s, so a counter costs a
 //    store-acknowledge, an atomic and a second round trip for the data.  Instead each
 //    produced value travels with its own completion flag: a 64-bit word holding the
-//    fp32 value and the step's epoch, stored and polled with device-scope (sc1)
-//    accesses.  A consumer is ready when every word it needs carries the current
-//    epoch, so one store and one poll cover data and signal.  The step's last CU
-//    (an atomic ticket, the one counter kept) advances the epoch for the next step.
+//    fp32 value and the step's epoch, stored and polled with device-scope accesses.
+//    A consumer is ready when every word it needs carries the current epoch.  The
+//    step's last CU (an atomic ticket, the one counter kept) advances the epoch.
 //  * A leader wave per CU does the waiting: it polls the inputs of the next
-//    instruction, applies RMSNorm / RoPE, stages the fp32 activation vector in LDS
-//    and releases the compute waves, which then only touch LDS and store results.
-//  * The article's 4-chunk MLP intermediate: the down projection is issued as 4
-//    K-chunks, each waiting only for its quarter of SiLU(gate)*up.
+//    instruction, applies RMSNorm / RoPE and stages the fp32 activation vector into
+//    one of MK_NACT LDS slots, so it can prepare instruction i+1 while the compute
+//    waves still work on instruction i.
+//  * The model's widths are template parameters: indices are compile-time arithmetic
+//    and loops have fixed trip counts.
+//  * The article's 4-chunk MLP intermediate: the down projection is issued as K-chunks,
+//    each waiting only for its part of SiLU(gate)*up.
 //
 // Every wait is bounded (watchdog); on expiry the wave records MK_ETIMEOUT, drains
 // its outstanding loads and exits, and the other waves follow.
@@ -44,8 +45,7 @@ namespace mkdev {
 typedef __attribute__((address_space(3))) char lds_char;
 typedef unsigned long long u64;
 // Read-only tables are read through the constant address space so that the compiler
-// uses scalar loads: a vector load in a compute wave would make the compiler wait
-// for every page load in flight before using it.
+// uses scalar loads.
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef const __attribute__((address_space(4))) MkInstr* cinstr_t;
 typedef const __attribute__((address_space(4))) MkLayerPtrs* clayers_t;
@@ -56,21 +56,48 @@ typedef const MkLayerPtrs* clayers_t;
 typedef const int32_t* cint_t;
 #endif
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// ------------------------------------------------------------------ model shape
+// Widths of one Llama-style decoder.  NCH: K-chunks of the down projection.
+template <int D_, int HQ_, int HKV_, int HD_, int F_, int NCH_>
+struct Shape {
+  static constexpr int D = D_, HQ = HQ_, HKV = HKV_, HD = HD_, F = F_, NCH = NCH_;
+  static constexpr int HPG = HQ / HKV, NQ = HQ * HD, NKV = HKV * HD, NQKV = NQ + 2 * NKV;
+  static constexpr int KC = F / NCH;                  // width of one down chunk
+  static constexpr int GRP = (HPG + 2) * HD;          // q heads | k | v of one KV group
+  static constexpr int ACT = cmax(cmax(D, NQ), cmax(KC, GRP));   // floats of one staged vector
+  static constexpr int PPP = MK_PAGE_BYTES / (4 * HD);           // cached positions per page
+  static_assert(D % 128 == 0 && NQ % 64 == 0 && KC % 64 == 0 && GRP % 64 == 0, "widths");
+  static_assert(HD == 64 || HD == 128, "head_dim");
+  static_assert(NCH >= 1 && NCH <= MK_MAX_NCH, "down chunks");
+};
+
+// LDS of one work-group (the page ring is a separate array).
+template <class S>
 struct __align__(16) MkShared {
-  float act[MK_ACT_FLOATS];                 // staged activation vector of the instruction
-  char pages[MK_PAGES_BYTES];               // page ring (nslot pages)
-  float xres[MK_MAX_RES_ROWS];              // x rows this CU's next residual adds to
-  float rowacc[MK_MAX_RES_ROWS];            // DOWN partial sums over the K-chunks
-  float rowres[MK_NC][64];                  // row results of the page being finished
+  float act[MK_NACT][S::ACT];               // staged activation vectors (ring)
+  float part[MK_NC][S::HPG][S::HD + 2];     // attention partials (m, l, o) per compute wave
+  float xres[2][MK_MAX_RES_ROWS];           // x rows for the residual of O (0) and DOWN (1)
+  float dpart[MK_MAX_NCH][MK_MAX_RES_ROWS]; // down-projection partial sums per chunk
   u64 amax[MK_NC];                          // per-wave argmax keys (LM head)
   int done[MK_NC];                          // instructions finished, per compute wave
-  uint16_t gain[MK_ACT_FLOATS];             // RMSNorm gains of the instruction being staged
   int full[MK_MAX_SLOTS];                   // ring slot holds page k once full == k + 1
   int freed[MK_MAX_SLOTS];                  // ring slot's page k consumed once freed == k + 1
   int act_seq;                              // instructions staged by the leader
   int abort_flag;
   uint32_t epoch;                           // tag of this step's words
   int token;                                // input token (validated)
+};
+
+// Pages in the LDS ring: what is left of 160 KiB, a multiple of MK_NL.
+template <class S>
+struct Ring {
+  static constexpr int FIXED = (int)sizeof(MkShared<S>) + 256;
+  static constexpr int NSLOT_RAW = (160 * 1024 - FIXED) / MK_PAGE_BYTES;
+  static constexpr int NSLOT = (NSLOT_RAW > MK_MAX_SLOTS ? MK_MAX_SLOTS : NSLOT_RAW) / MK_NL * MK_NL;
+  static_assert(NSLOT >= 2 * MK_NL, "LDS");
 };
 
 // ------------------------------------------------------------------ small helpers
@@ -80,30 +107,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // HBM -> LDS, 16 bytes per lane: lane i lands at lds + 16*i.  Issued through inline
 // assembly so that the compiler does not add a wait for it before later LDS accesses.
+// Non-temporal: each weight byte is read once per step and should not displace
+// anything in L2.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :: "v"(g), "s"(l) : "memory", "m0");
 }
 
 #define MK_VMCNT_CASE(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
-// Wait until at most n vector-memory operations of this wave are outstanding.
+// Wait until at most n vector-memory operations of this wave are outstanding (n is a
+// multiple of 16 below 64: pages are 16 loads).
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
-    MK_VMCNT_CASE(0) MK_VMCNT_CASE(1) MK_VMCNT_CASE(2) MK_VMCNT_CASE(3) MK_VMCNT_CASE(4)
-    MK_VMCNT_CASE(5) MK_VMCNT_CASE(6) MK_VMCNT_CASE(7) MK_VMCNT_CASE(8) MK_VMCNT_CASE(9)
-    MK_VMCNT_CASE(10) MK_VMCNT_CASE(11) MK_VMCNT_CASE(12) MK_VMCNT_CASE(13) MK_VMCNT_CASE(14)
-    MK_VMCNT_CASE(15) MK_VMCNT_CASE(16) MK_VMCNT_CASE(17) MK_VMCNT_CASE(18) MK_VMCNT_CASE(19)
-    MK_VMCNT_CASE(20) MK_VMCNT_CASE(21) MK_VMCNT_CASE(22) MK_VMCNT_CASE(23) MK_VMCNT_CASE(24)
-    MK_VMCNT_CASE(25) MK_VMCNT_CASE(26) MK_VMCNT_CASE(27) MK_VMCNT_CASE(28) MK_VMCNT_CASE(29)
-    MK_VMCNT_CASE(30) MK_VMCNT_CASE(31) MK_VMCNT_CASE(32) MK_VMCNT_CASE(33) MK_VMCNT_CASE(34)
-    MK_VMCNT_CASE(35) MK_VMCNT_CASE(36) MK_VMCNT_CASE(37) MK_VMCNT_CASE(38) MK_VMCNT_CASE(39)
-    MK_VMCNT_CASE(40) MK_VMCNT_CASE(41) MK_VMCNT_CASE(42) MK_VMCNT_CASE(43) MK_VMCNT_CASE(44)
-    MK_VMCNT_CASE(45) MK_VMCNT_CASE(46) MK_VMCNT_CASE(47) MK_VMCNT_CASE(48) MK_VMCNT_CASE(49)
-    MK_VMCNT_CASE(50) MK_VMCNT_CASE(51) MK_VMCNT_CASE(52) MK_VMCNT_CASE(53) MK_VMCNT_CASE(54)
-    MK_VMCNT_CASE(55) MK_VMCNT_CASE(56) MK_VMCNT_CASE(57) MK_VMCNT_CASE(58) MK_VMCNT_CASE(59)
-    MK_VMCNT_CASE(60) MK_VMCNT_CASE(61) MK_VMCNT_CASE(62)
-    default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
+    MK_VMCNT_CASE(16) MK_VMCNT_CASE(32) MK_VMCNT_CASE(48)
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
 #undef MK_VMCNT_CASE
@@ -116,7 +134,6 @@ __device__ __forceinline__ int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
-
 // Ties a loaded value to this point of the program, so that the compiler cannot sink
 // the load into the branch that uses it (which would make one round trip per load).
 __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
@@ -163,7 +180,7 @@ __device__ __forceinline__ float dot8(uint4 w, const float* a, float acc) {
   return acc;
 }
 
-// ------------------------------------------------------------------ reductions (DPP)
+// ------------------------------------------------------------------ reductions
 // Cross-lane sums through DPP moves (no LDS round trip).  sumN leaves the sum of each
 // aligned group of N lanes in every lane of the group.
 template <int CTRL, int ROW_MASK = 0xf>
@@ -198,11 +215,45 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<0x143, 0xc>(v, -INFINITY));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-// Sum within aligned groups of g lanes (g a power of two <= 64), by lane swaps.
-__device__ __forceinline__ float group_sum(float v, int g) {
-  for (int off = g >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+// Sum within aligned groups of G lanes (G a power of two <= 64), in every lane.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 16) v = sum16(v);
+  else if constexpr (G == 8) v = sum8(v);
+  else {
+    if constexpr (G >= 2) v += dpp_f<0xB1>(v, 0.f);
+    if constexpr (G >= 4) v += dpp_f<0x4E>(v, 0.f);
+  }
+  if constexpr (G >= 32) v += __shfl_xor(v, 16);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32);
   return v;
 }
+
+// N values per lane, each to be summed over aligned groups of G lanes (N <= G, both
+// powers of two).  Halving steps hand half of the values to the partner lane, so that
+// after log2(N) steps each lane holds one partial; the rest of the group is then summed.
+// Value n ends in the lanes l with (l % G) / (G / N) == n.
+template <int N, int G>
+__device__ __forceinline__ float reduce_rows(float (&v)[N], int lane) {
+  static_assert(N <= G, "reduce_rows");
+#pragma unroll
+  for (int s = 0; s < ilog2(N); ++s) {
+    const int dist = G >> (s + 1);
+    const int n = N >> s;
+    // Selects through a bit mask: a lane-dependent choice between two array elements
+    // must not become an indexed (private memory) access.
+    const uint32_t m = (lane & dist) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + n / 2]);
+      const float keep = __uint_as_float((hi & m) | (lo & ~m));
+      const float send = __uint_as_float((lo & m) | (hi & ~m));
+      v[i] = keep + __shfl_xor(send, dist);
+    }
+  }
+  return group_sum<G / N>(v[0]);
+}
+
 __device__ __forceinline__ u64 wave_max_u64(u64 v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -219,170 +270,176 @@ __device__ __forceinline__ u64 amax_key(float v, uint32_t idx) {
   return ((u64)u << 32) | (u64)(0xffffffffu - idx);
 }
 
-__device__ __forceinline__ void trace_mark(const MkParams& p, int cu, int i, int slot, int lane) {
+__device__ __forceinline__ void trace_mark(const MkParams& p, int i, int slot, int lane) {
   if (p.trace && lane == 0 && i < p.trace_len)
-    p.trace[((size_t)cu * p.trace_len + i) * MK_TRACE_SLOTS + slot] = __builtin_amdgcn_s_memrealtime();
+    p.trace[((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
 // ------------------------------------------------------------------ step geometry
 struct StepGeo {
-  int pos, s_eff, chunk, ppp;   // attention split of keys 0..pos
+  int pos, s_eff, chunk;   // attention split of keys 0..pos
 };
 
+template <class S>
 __device__ __forceinline__ StepGeo step_geo(const MkParams& p, int pos) {
   StepGeo g;
   g.pos = pos;
-  g.ppp = p.page_bytes / (4 * p.hd);       // key+value positions per page
   const int nk = pos + 1;
   int chunk = (nk + p.s_max - 1) / p.s_max;
   if (chunk < p.min_chunk) chunk = p.min_chunk;
-  chunk = (chunk + g.ppp - 1) / g.ppp * g.ppp;
+  chunk = (chunk + S::PPP - 1) / S::PPP * S::PPP;
   g.chunk = chunk;
   g.s_eff = (nk + chunk - 1) / chunk;
   return g;
 }
 
-// Keys [j0, j1) of split s; the cached part (read from the cache) is [j0, min(j1, pos)).
-__device__ __forceinline__ void attn_range(const StepGeo& g, int s, int* j0, int* j1, int* cached_end) {
-  const int nk = g.pos + 1;
-  *j0 = s * g.chunk;
-  *j1 = min(nk, (s + 1) * g.chunk);
-  *cached_end = min(*j1, g.pos);
-}
+// ------------------------------------------------------------------ page geometry
+// Rows of SEG bytes in a 16 KiB page.  Wide rows (>= 1 KiB) are KU whole units of
+// 1 KiB, lane l holding bytes 16l.. of each unit; narrow rows share a unit, LPR lanes
+// per row.
+template <int SEG>
+struct RowGeo {
+  static constexpr bool WIDE = SEG >= 1024;
+  static constexpr int KU = WIDE ? SEG / 1024 : 1;        // units per row
+  static constexpr int LPR = WIDE ? 64 : SEG / 16;        // lanes per row within a unit
+  static constexpr int RPU = WIDE ? 1 : 64 / LPR;         // rows per unit
+  static constexpr int RPP = WIDE ? 16 / KU : 16 * RPU;   // rows per page
+  static constexpr int USED = WIDE ? RPP * KU : 16;       // units carrying payload
+  static constexpr int NV = WIDE ? RPP : 16;              // partial sums per lane per page
+  static constexpr int G = WIDE ? 64 : LPR;               // lanes a partial is summed over
+  static_assert(WIDE ? (SEG % 1024 == 0 && SEG <= 8192) : (SEG == 256 || SEG == 512), "row length");
+};
 
 // An instruction decoded once: everything its pages need, wave-uniform.
 struct Dec {
-  int op, layer, r0, n, k0, kn, a, b;
+  int op, layer, r0, n, k0, a, b;
   int np;            // pages of the instruction on this CU
-  int seg;           // bytes of one row segment
-  int rpp;           // rows per page (GATEUP: gate/up pairs per page)
-  int upr;           // 1 KiB units per row, or 0 when a row is shorter than 1 KiB
-  int lpr_sh;        // log2(lanes per row) when a row is shorter than 1 KiB
-  int s1, s2;        // QKV: rows below s1 come from m0, below s2 from m1, the rest from m2
+  int rpp;           // rows per page (GATEUP: gate and up rows, two per feature)
   const char* m0;    // row 0 of each source matrix, input column k0 applied (bytes)
   const char* m1;
   const char* m2;
-  long long stride;  // bytes between rows
   int j0, ce;        // ATTN: cached keys [j0, ce); m0 / m1 = K / V of (layer, kv head) at key 0
 };
 
+template <class S>
 __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, const StepGeo& g) {
   Dec d;
-  d.op = in.op; d.layer = in.layer; d.r0 = in.r0; d.n = in.n; d.k0 = in.k0; d.kn = in.kn; d.a = in.a; d.b = in.b;
-  d.s1 = d.s2 = 0;
+  d.op = in.op; d.layer = in.layer; d.r0 = in.r0; d.n = in.n; d.k0 = in.k0; d.a = in.a; d.b = in.b;
   d.m0 = d.m1 = d.m2 = nullptr;
-  d.upr = d.lpr_sh = 0;
-  d.seg = d.rpp = 0;
   d.j0 = d.ce = 0;
-  d.stride = 0;
+  d.rpp = 0;
   if (in.op == MK_OP_ATTN) {
     d.np = 0;
     if (in.b < g.s_eff) {
-      int j1;
-      attn_range(g, in.b, &d.j0, &j1, &d.ce);
+      d.j0 = in.b * g.chunk;
+      d.ce = min(min(g.pos + 1, (in.b + 1) * g.chunk), g.pos);   // the current key is not in the cache yet
       const int cached = d.ce - d.j0;
-      d.np = cached > 0 ? (cached + g.ppp - 1) / g.ppp : 0;
+      d.np = cached > 0 ? (cached + S::PPP - 1) / S::PPP : 0;
     }
-    const size_t head = ((size_t)(in.layer * 2) * p.hkv + in.a) * p.max_ctx;
-    d.m0 = (const char*)(p.kv + head * p.hd);
-    d.m1 = (const char*)(p.kv + (head + (size_t)p.hkv * p.max_ctx) * p.hd);
+    const size_t head = ((size_t)(in.layer * 2) * S::HKV + in.a) * p.max_ctx;
+    d.m0 = (const char*)(p.kv + head * S::HD);
+    d.m1 = (const char*)(p.kv + (head + (size_t)S::HKV * p.max_ctx) * S::HD);
     return d;
   }
-  d.seg = 2 * in.kn;
-  d.rpp = in.op == MK_OP_GATEUP ? p.page_bytes / (2 * d.seg) : p.page_bytes / d.seg;
-  d.np = (in.n + d.rpp - 1) / d.rpp;
-  if (d.seg >= 1024) d.upr = d.seg >> 10;
-  else d.lpr_sh = 31 - __builtin_clz((unsigned)(d.seg >> 4));
-  const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
+  const int seg = in.op == MK_OP_O ? 2 * S::NQ : in.op == MK_OP_DOWN ? 2 * S::KC : 2 * S::D;
+  d.rpp = MK_PAGE_BYTES / seg;
+  const int rows = in.op == MK_OP_GATEUP ? 2 * in.n : in.n;
+  d.np = (rows + d.rpp - 1) / d.rpp;
   // Plain selects, not a switch: a switch over runtime values becomes a table in
-  // private memory, read with vector loads.
+  // private memory.
+  const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
   const bool qkv = in.op == MK_OP_QKV, gu = in.op == MK_OP_GATEUP, o = in.op == MK_OP_O,
              dn = in.op == MK_OP_DOWN;
-  const uint16_t* a0 = qkv ? L.wq : gu ? L.wg : o ? L.wo : dn ? L.wd : p.lm_head;
-  const uint16_t* a1 = qkv ? L.wk : gu ? L.wu : nullptr;
-  const uint16_t* a2 = qkv ? L.wv : nullptr;
-  d.stride = 2LL * (o ? p.nq : dn ? p.F : p.d);
-  if (qkv) {
-    d.s1 = p.nq;
-    d.s2 = p.nq + p.nkv;
-  }
-  d.m0 = (const char*)(a0 + in.k0);
-  d.m1 = a1 ? (const char*)(a1 + in.k0) : d.m0;
-  d.m2 = a2 ? (const char*)(a2 + in.k0) : d.m0;
+  const uint16_t* a0 = qkv ? L.wq : gu ? L.wg : o ? L.wo : dn ? L.wd + in.k0 : p.lm_head;
+  d.m0 = (const char*)a0;
+  d.m1 = (const char*)(qkv ? L.wk : gu ? L.wu : a0);
+  d.m2 = (const char*)(qkv ? L.wv : a0);
   return d;
 }
 
-// Row j of page `first`: the page holds rows first.. of the instruction, or for GATEUP the
-// interleaved pairs gate(f), up(f), gate(f+1), up(f+1), ... with f = r0 + first.
-__device__ __forceinline__ const char* page_row(const Dec& d, int first, int j) {
+// Address of row j (page-relative) of page `pg`.  GATEUP pages interleave gate(f), up(f),
+// gate(f+1), up(f+1), ...; QKV rows run through Wq, then Wk, then Wv.
+template <class S>
+__device__ __forceinline__ const char* row_ptr(const Dec& d, int pg, int j) {
+  const int pr = pg * d.rpp + j;   // row of the instruction
   if (d.op == MK_OP_GATEUP) {
-    const long long f = d.r0 + first + (j >> 1);
-    return ((j & 1) ? d.m1 : d.m0) + f * d.stride;
+    const long long f = d.r0 + (pr >> 1);
+    return ((pr & 1) ? d.m1 : d.m0) + f * (2LL * S::D);
   }
-  const int gr = d.r0 + first + j;
+  const int gr = d.r0 + pr;
   if (d.op == MK_OP_QKV) {
-    if (gr >= d.s2) return d.m2 + (long long)(gr - d.s2) * d.stride;
-    if (gr >= d.s1) return d.m1 + (long long)(gr - d.s1) * d.stride;
+    if (gr >= S::NQ + S::NKV) return d.m2 + (long long)(gr - S::NQ - S::NKV) * (2 * S::D);
+    if (gr >= S::NQ) return d.m1 + (long long)(gr - S::NQ) * (2 * S::D);
+    return d.m0 + (long long)gr * (2 * S::D);
   }
-  return d.m0 + (long long)gr * d.stride;
+  if (d.op == MK_OP_O) return d.m0 + (long long)gr * (2 * S::NQ);
+  if (d.op == MK_OP_DOWN) return d.m0 + (long long)gr * (2 * S::F);
+  return d.m0 + (long long)gr * (2 * S::D);
 }
 
-// Issue the DMA of page pg into the LDS page at `slot`: always `lpp` loads of 1 KiB so
-// the wave's vmcnt moves in multiples of lpp; loads past the payload re-read valid bytes.
-__device__ __forceinline__ void issue_page(const Dec& d, int pg, int ppp, int hd, int lpp, uint32_t slot,
-                                           int lane) {
+// Issue the DMA of page pg into the LDS page at `slot`: always 16 loads of 1 KiB so the
+// wave's vmcnt moves in steps of 16; loads past the payload re-read valid bytes.
+template <class S, int SEG>
+__device__ __forceinline__ void issue_rows(const Dec& d, int pg, uint32_t slot, int lane) {
+  using R = RowGeo<SEG>;
+  const int rows = (d.op == MK_OP_GATEUP ? 2 * d.n : d.n) - pg * d.rpp;   // rows from this page on
+  if constexpr (R::WIDE) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = u / R::KU, c = u % R::KU;
+      const bool real = u < R::USED && j < rows;
+      const char* rb = row_ptr<S>(d, pg, real ? j : 0);
+      dma16(rb + (real ? c * 1024 : 0) + lane * 16, slot + u * 1024);
+    }
+  } else {
+    const int jl = lane / R::LPR, cl = lane % R::LPR;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = u * R::RPU + jl;
+      dma16(row_ptr<S>(d, pg, j < rows ? j : 0) + cl * 16, slot + u * 1024);
+    }
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void issue_page(const Dec& d, int pg, uint32_t slot, int lane) {
   if (d.op == MK_OP_ATTN) {
-    const int q0 = d.j0 + pg * ppp;
-    const int np = min(ppp, d.ce - q0);
-    const int rowb = 2 * hd;
-    const int kbytes = np * rowb;
-    const char* kb = d.m0 + (size_t)q0 * rowb;
-    const char* vb = d.m1 + (size_t)q0 * rowb;
-    for (int u = 0; u < lpp; ++u) {
+    constexpr int ROWB = 2 * S::HD;
+    const int q0 = d.j0 + pg * S::PPP;
+    const int np = min(S::PPP, d.ce - q0);
+    const int kbytes = np * ROWB;
+    const char* kb = d.m0 + (size_t)q0 * ROWB;
+    const char* vb = d.m1 + (size_t)q0 * ROWB;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
       const int o = u * 1024 + lane * 16;
       const char* a = o < kbytes ? kb + o : (o < 2 * kbytes ? vb + (o - kbytes) : kb);
       dma16(a, slot + u * 1024);
     }
     return;
   }
-  const int first = pg * d.rpp;
-  const int m = min(d.rpp, d.n - first);
-  const int rows = d.op == MK_OP_GATEUP ? 2 * m : m;
-  if (d.upr) {
-    // One row base per row (a few scalar ops), then its 1 KiB units by plain adds.
-    uint32_t dst = slot;
-    int u = 0;
-    for (int j = 0; j < rows; ++j) {
-      const char* rb = page_row(d, first, j) + lane * 16;
-      for (int c = 0; c < d.upr; ++c, ++u, dst += 1024) dma16(rb + c * 1024, dst);
-    }
-    const char* dummy = d.m0 + lane * 16;   // keeps the load count at lpp
-    for (; u < lpp; ++u, dst += 1024) dma16(dummy, dst);
-  } else {
-    const int rpu = 64 >> d.lpr_sh;
-    const int cl = lane & ((1 << d.lpr_sh) - 1);
-    for (int u = 0; u < lpp; ++u) {
-      const int jl = u * rpu + (lane >> d.lpr_sh);
-      dma16(page_row(d, first, jl < rows ? jl : 0) + cl * 16, slot + u * 1024);
-    }
-  }
+  if (d.op == MK_OP_O) issue_rows<S, 2 * S::NQ>(d, pg, slot, lane);
+  else if (d.op == MK_OP_DOWN) issue_rows<S, 2 * S::KC>(d, pg, slot, lane);
+  else issue_rows<S, 2 * S::D>(d, pg, slot, lane);
 }
 
 // ------------------------------------------------------------------ waits and aborts
-__device__ __forceinline__ void raise_error(const MkParams& p, MkShared& sh, int code) {
+template <class S>
+__device__ __forceinline__ void raise_error(const MkParams& p, MkShared<S>& sh, int code) {
   atomicCAS(&p.ctrl->error, 0, code);
   lds_store(&sh.abort_flag, 1);
 }
 
-// Compute waves never read the global error word (a vector load would wait for their
-// page loads); they follow the LDS abort flag and their own clock.
+// Compute waves never read the global error word; they follow the LDS abort flag and
+// their own clock.
+template <class S>
 struct Waiter {
   long long t0;
   int n;
   bool global_check;
   __device__ __forceinline__ Waiter(bool leader) : t0(__builtin_amdgcn_s_memrealtime()), n(0), global_check(leader) {}
   // true when the wait must be abandoned
-  __device__ __forceinline__ bool tick(const MkParams& p, MkShared& sh) {
+  __device__ __forceinline__ bool tick(const MkParams& p, MkShared<S>& sh) {
     __builtin_amdgcn_s_sleep(1);
     if (lds_load(&sh.abort_flag)) return true;
     if ((++n & 63) == 0) {
@@ -401,217 +458,201 @@ struct Waiter {
 };
 
 // Wait until *flag >= target (LDS).  False if abandoned.
-__device__ __forceinline__ bool wait_flag(const MkParams& p, MkShared& sh, const int* flag, int target,
+template <class S>
+__device__ __forceinline__ bool wait_flag(const MkParams& p, MkShared<S>& sh, const int* flag, int target,
                                           bool leader) {
   if (lds_load(flag) >= target) { compiler_fence(); return true; }
-  Waiter wt(leader);
+  Waiter<S> wt(leader);
   while (lds_load(flag) < target)
     if (wt.tick(p, sh)) return false;
   compiler_fence();
   return true;
 }
 
-__device__ __forceinline__ bool wait_all_done(const MkParams& p, MkShared& sh, int target) {
+template <class S>
+__device__ __forceinline__ bool wait_all_done(const MkParams& p, MkShared<S>& sh, int target, bool leader) {
   for (int w = 0; w < MK_NC; ++w)
-    if (!wait_flag(p, sh, &sh.done[w], target, true)) return false;
+    if (!wait_flag(p, sh, &sh.done[w], target, leader)) return false;
   return true;
 }
 
 // ------------------------------------------------------------------ page ring
 // The pages of the CU's whole list, in list order, are numbered k = 0, 1, ...; page k
-// lives in ring slot k % nslot, is issued by loader wave k % MK_NL and consumed by
+// lives in ring slot k % NSLOT, is issued by loader wave k % MK_NL and consumed by
 // compute wave k % MK_NC.  LDS flags: full[slot] = k + 1 once page k has landed,
-// freed[slot] = k + 1 once its compute wave has read it.  nslot is a multiple of
+// freed[slot] = k + 1 once its compute wave has read it.  NSLOT is a multiple of
 // MK_NL, so the page a loader waits to be freed is one it issued itself.
 __device__ __forceinline__ int first_of(int who, int base, int period) {
   return ((who - base) % period + period) % period;
 }
 
 // Loader wave l.  It publishes its pages in order, each once vmcnt shows it complete,
-// keeping at most D of them unpublished (vmcnt counts to 63).  While it waits for a
-// slot still in use it keeps publishing what it has in flight: a compute wave may be
-// waiting for one of those pages.
-__device__ __forceinline__ void loader_wave(const MkParams& p, MkShared& sh, cinstr_t list, int nins,
-                                            const StepGeo& g, int l, int lane) {
-  const int nslot = p.nslot, lpp = p.lpp, pb = p.page_bytes;
-  const uint32_t ring = lds_addr(sh.pages);
-  const int D = min(8, min(nslot / MK_NL, 63 / lpp + 1));
+// keeping at most DEPTH of them unpublished.  While it waits for a slot still in use it
+// keeps publishing what it has in flight: a compute wave may be waiting for one of them.
+template <class S>
+__device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, char* ring_base, cinstr_t list,
+                                            int nins, const StepGeo& g, int l, int lane) {
+  constexpr int NSLOT = Ring<S>::NSLOT;
+  constexpr int DEPTH = NSLOT / MK_NL < 4 ? NSLOT / MK_NL : 4;   // 16 loads per page, vmcnt <= 63
+  const uint32_t ring = lds_addr(ring_base);
   int oldest = 0, pend = 0;   // own pages issued and not yet published: oldest, then every MK_NL-th
   int base = 0;
   for (int i = 0; i < nins; ++i) {
-    const Dec d = decode(p, list[i], g);
+    const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
     for (int pg = first_of(l, base, MK_NL); pg < d.np; pg += MK_NL) {
       const int k = base + pg;
-      const int slot = k % nslot;
+      const int slot = k % NSLOT;
       // Slot still in use: publish own pages as they land (oldest first) while waiting.
-      while (lds_load(&sh.freed[slot]) < k - nslot + 1) {
+      while (lds_load(&sh.freed[slot]) < k - NSLOT + 1) {
         if (pend == 0) {
-          if (!wait_flag(p, sh, &sh.freed[slot], k - nslot + 1, false)) {
-            wait_vmcnt(0);   // nothing may land in LDS after the wave has left
+          if (!wait_flag(p, sh, &sh.freed[slot], k - NSLOT + 1, false)) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // nothing may land in LDS after the wave has left
             return;
           }
           break;
         }
-        wait_vmcnt((pend - 1) * lpp);
-        if (lane == 0) lds_store(&sh.full[oldest % nslot], oldest + 1);
+        wait_vmcnt((pend - 1) * 16);
+        if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
         oldest += MK_NL;
         --pend;
       }
-      issue_page(d, pg, g.ppp, p.hd, lpp, ring + (uint32_t)(slot * pb), lane);
+      issue_page<S>(d, pg, ring + (uint32_t)(slot * MK_PAGE_BYTES), lane);
       if (pend == 0) oldest = k;
       ++pend;
-      if (pend == D) {   // the oldest is complete once at most (D - 1) pages are outstanding
-        wait_vmcnt((D - 1) * lpp);
-        if (lane == 0) lds_store(&sh.full[oldest % nslot], oldest + 1);
+      if (pend == DEPTH) {   // the oldest is complete once at most (DEPTH - 1) pages are outstanding
+        wait_vmcnt((DEPTH - 1) * 16);
+        if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
         oldest += MK_NL;
         --pend;
       }
     }
     base += d.np;
   }
-  wait_vmcnt(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   for (; pend > 0; --pend, oldest += MK_NL)
-    if (lane == 0) lds_store(&sh.full[oldest % nslot], oldest + 1);
+    if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
 }
 
 // Page k for a compute wave, once it has landed (nullptr if the wait was abandoned).
-__device__ __forceinline__ const char* page_wait(const MkParams& p, MkShared& sh, int k) {
-  const int slot = k % p.nslot;
+template <class S>
+__device__ __forceinline__ const char* page_wait(const MkParams& p, MkShared<S>& sh, const char* ring_base, int k) {
+  const int slot = k % Ring<S>::NSLOT;
   if (!wait_flag(p, sh, &sh.full[slot], k + 1, false)) return nullptr;
-  return sh.pages + slot * p.page_bytes;
+  return ring_base + slot * MK_PAGE_BYTES;
 }
 // The wave has finished reading page k: once its LDS reads have returned the loader
 // may overwrite the slot.
-__device__ __forceinline__ void page_free(const MkParams& p, MkShared& sh, int k, int lane) {
+template <class S>
+__device__ __forceinline__ void page_free(MkShared<S>& sh, int k, int lane) {
   lds_fence();
-  if (lane == 0) lds_store(&sh.freed[k % p.nslot], k + 1);
+  if (lane == 0) lds_store(&sh.freed[k % Ring<S>::NSLOT], k + 1);
 }
 
 // ------------------------------------------------------------------ compute waves
 // Group-major index of a raw q/k/v row: [kv head][q heads of the group | k | v][hd].
-__device__ __forceinline__ int qkv_index(const MkParams& p, int row) {
-  const int grp = (p.hpg + 2) * p.hd;
-  if (row < p.nq) {
-    const int h = row / p.hd;
-    return (h / p.hpg) * grp + (h % p.hpg) * p.hd + (row - h * p.hd);
+template <class S>
+__device__ __forceinline__ int qkv_index(int row) {
+  if (row < S::NQ) {
+    const int h = row / S::HD;
+    return (h / S::HPG) * S::GRP + (h % S::HPG) * S::HD + (row % S::HD);
   }
-  if (row < p.nq + p.nkv) {
-    const int r = row - p.nq;
-    return (r / p.hd) * grp + p.hpg * p.hd + (r % p.hd);
+  if (row < S::NQ + S::NKV) {
+    const int r = row - S::NQ;
+    return (r / S::HD) * S::GRP + S::HPG * S::HD + (r % S::HD);
   }
-  const int r = row - p.nq - p.nkv;
-  return (r / p.hd) * grp + (p.hpg + 1) * p.hd + (r % p.hd);
+  const int r = row - S::NQ - S::NKV;
+  return (r / S::HD) * S::GRP + (S::HPG + 1) * S::HD + (r % S::HD);
 }
 
-// Finish one output row (value v, uniform over the wave; lane 0 stores).
-__device__ __forceinline__ void row_epilogue(const MkParams& p, MkShared& sh, const Dec& d, int gr, float v,
-                                             int lane, uint32_t epoch, u64* best) {
+// One GEMV instruction on the wave's pages.  The lane's slice of the activation stays in
+// registers for the whole instruction.  Per page: every row's partial dot product, one
+// combined cross-lane reduction for all rows of the page, then the rows' epilogues run
+// in parallel in the lanes that hold them.
+template <class S, int SEG>
+__device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
+                                     const float* act, int base, int w, int lane, uint32_t epoch, u64* best) {
+  using R = RowGeo<SEG>;
+  // The activation slice is kept in registers for rows of up to 4 KiB; longer rows read
+  // it from LDS per unit (it would otherwise take 64 registers).
+  constexpr bool AREG = R::KU <= 4;
+  constexpr int AU = AREG ? R::KU : 1;
+  float av[AU][8];
+  if constexpr (AREG) {
+#pragma unroll
+    for (int u = 0; u < R::KU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        av[u][e] = act[(R::WIDE ? u * 512 + lane * 8 : (lane % R::LPR) * 8) + e];
+  }
+  const int rows_total = d.op == MK_OP_GATEUP ? 2 * d.n : d.n;
   const int l = d.layer;
-  switch (d.op) {
-    case MK_OP_QKV:
-      if (lane == 0) ll_store(p.ll_qkv + (size_t)l * p.nqkv + qkv_index(p, gr), v, epoch);
-      break;
-    case MK_OP_O:
-      if (lane == 0) ll_store(p.ll_x + (size_t)(2 * l + 1) * p.d + gr, sh.xres[gr - d.r0] + v, epoch);
-      break;
-    case MK_OP_DOWN: {
-      const int k = gr - d.r0;
-      const float acc = (d.a == 0 ? 0.f : sh.rowacc[k]) + v;
-      if (d.a + 1 < d.b) {
-        if (lane == 0) sh.rowacc[k] = acc;
-      } else if (lane == 0) {
-        ll_store(p.ll_x + (size_t)(2 * l + 2) * p.d + gr, sh.xres[k] + acc, epoch);
-      }
-      break;
-    }
-    default: {  // MK_OP_LMHEAD
-      if (lane == 0) p.logits[gr] = v;
-      const u64 key = amax_key(v, (uint32_t)gr);
-      if (key > *best) *best = key;
-      break;
-    }
-  }
-}
-
-__device__ __forceinline__ void gateup_epilogue(const MkParams& p, const Dec& d, int f, float gt, float up,
-                                                int lane, uint32_t epoch) {
-  const float a = (gt / (1.0f + __expf(-gt))) * up;
-  if (lane == 0) ll_store(p.ll_a + (size_t)d.layer * p.F + f, a, epoch);
-}
-
-// Rows of at least 1 KiB: the lane's slice of the activation stays in registers for the
-// whole instruction; each row is UPR units of 1 KiB, lane l holding bytes 16l.. of each.
-template <int UPR>
-__device__ __forceinline__ float row_dot(const char* page, int j, const float (&av)[UPR][8], int lane) {
-  uint4 wv[UPR];   // all units' LDS reads first, so their latency overlaps
-#pragma unroll
-  for (int u = 0; u < UPR; ++u) wv[u] = *(const uint4*)(page + (j * UPR + u) * 1024 + lane * 16);
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < UPR; ++u) acc = dot8(wv[u], av[u], acc);
-  return acc;
-}
-
-template <int UPR>
-__device__ __forceinline__ bool gemv_wide(const MkParams& p, MkShared& sh, const Dec& d, int base, int w, int lane,
-                                          uint32_t epoch, u64* best) {
-  float av[UPR][8];
-#pragma unroll
-  for (int u = 0; u < UPR; ++u)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) av[u][e] = sh.act[u * 512 + lane * 8 + e];
   for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
-    const char* page = page_wait(p, sh, base + pg);
+    const char* page = page_wait<S>(p, sh, ring_base, base + pg);
     if (!page) return false;
-    const int first = pg * d.rpp;
-    const int m = min(d.rpp, d.n - first);
-    if (d.op == MK_OP_GATEUP) {
-      for (int j = 0; j < m; ++j) {
-        const float g = wave_sum(row_dot<UPR>(page, 2 * j, av, lane));
-        const float u = wave_sum(row_dot<UPR>(page, 2 * j + 1, av, lane));
-        gateup_epilogue(p, d, d.r0 + first + j, g, u, lane, epoch);
+    uint4 wv[R::USED];
+#pragma unroll
+    for (int u = 0; u < R::USED; ++u) wv[u] = *(const uint4*)(page + u * 1024 + lane * 16);
+    float acc[R::NV];
+    if constexpr (R::WIDE && AREG) {
+#pragma unroll
+      for (int j = 0; j < R::RPP; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < R::KU; ++u) a = dot8(wv[j * R::KU + u], av[u], a);
+        acc[j] = a;
+      }
+    } else if constexpr (R::WIDE) {
+#pragma unroll
+      for (int j = 0; j < R::RPP; ++j) acc[j] = 0.f;
+#pragma unroll
+      for (int u = 0; u < R::KU; ++u) {
+        const float4 x0 = *(const float4*)(act + u * 512 + lane * 8);
+        const float4 x1 = *(const float4*)(act + u * 512 + lane * 8 + 4);
+        const float a[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < R::RPP; ++j) acc[j] = dot8(wv[j * R::KU + u], a, acc[j]);
       }
     } else {
-      int j = 0;
-      for (; j + 1 < m; j += 2) {
-        const float v0 = wave_sum(row_dot<UPR>(page, j, av, lane));
-        const float v1 = wave_sum(row_dot<UPR>(page, j + 1, av, lane));
-        row_epilogue(p, sh, d, d.r0 + first + j, v0, lane, epoch, best);
-        row_epilogue(p, sh, d, d.r0 + first + j + 1, v1, lane, epoch, best);
-      }
-      if (j < m) row_epilogue(p, sh, d, d.r0 + first + j, wave_sum(row_dot<UPR>(page, j, av, lane)), lane, epoch, best);
-    }
-    page_free(p, sh, base + pg, lane);
-  }
-  return true;
-}
-
-// Rows shorter than 1 KiB (small models): several rows per 1 KiB unit, lpr lanes per row;
-// results go through LDS so that lane j can finish row j.
-__device__ __forceinline__ bool gemv_narrow(const MkParams& p, MkShared& sh, const Dec& d, int base, int w,
-                                            int lane, uint32_t epoch, u64* best) {
-  const int lpr = 1 << d.lpr_sh, rpu = 64 >> d.lpr_sh, c = lane & (lpr - 1);
-  float av[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) av[e] = sh.act[c * 8 + e];
-  float* res = sh.rowres[w];
-  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
-    const char* page = page_wait(p, sh, base + pg);
-    if (!page) return false;
-    const int first = pg * d.rpp;
-    const int m = min(d.rpp, d.n - first);
-    const int rows = d.op == MK_OP_GATEUP ? 2 * m : m;
-    for (int u = 0; u * rpu < rows; ++u) {
-      float acc = dot8(*(const uint4*)(page + u * 1024 + lane * 16), av, 0.f);
-      acc = group_sum(acc, lpr);
-      const int j = u * rpu + (lane >> d.lpr_sh);
-      if (c == 0 && j < rows) res[j] = acc;
+      for (int u = 0; u < 16; ++u) acc[u] = dot8(wv[u], av[0], 0.f);
     }
-    page_free(p, sh, base + pg, lane);
-    for (int j = 0; j < m; ++j) {
-      if (d.op == MK_OP_GATEUP) gateup_epilogue(p, d, d.r0 + first + j, res[2 * j], res[2 * j + 1], lane, epoch);
-      else row_epilogue(p, sh, d, d.r0 + first + j, res[j], lane, epoch, best);
+    page_free<S>(sh, base + pg, lane);
+    const float v = reduce_rows<R::NV, R::G>(acc, lane);
+    // The row this lane holds, relative to the page, and whether the lane stores it.
+    constexpr int SPAN = R::G / R::NV;                        // lanes holding one value
+    const int vi = (lane % R::G) / SPAN;                      // value index
+    const int j = R::WIDE ? vi : vi * R::RPU + lane / R::LPR;  // row in the page
+    const bool owner = (lane % SPAN) == 0;
+    const int pr = pg * d.rpp + j;                             // row of the instruction
+    const bool valid = owner && pr < rows_total;
+    if (d.op == MK_OP_GATEUP) {
+      constexpr int UP = R::WIDE ? SPAN : R::LPR;             // lane distance gate row -> up row
+      const float up = __shfl_down(v, UP);
+      if (valid && (pr & 1) == 0) {
+        const float a = (v / (1.0f + __expf(-v))) * up;
+        ll_store(p.ll_a + (size_t)l * S::F + d.r0 + (pr >> 1), a, epoch);
+      }
+    } else if (valid) {
+      const int gr = d.r0 + pr;
+      if (d.op == MK_OP_QKV) {
+        ll_store(p.ll_qkv + (size_t)l * S::NQKV + qkv_index<S>(gr), v, epoch);
+      } else if (d.op == MK_OP_O) {
+        ll_store(p.ll_x + (size_t)(2 * l + 1) * S::D + gr, sh.xres[0][pr] + v, epoch);
+      } else if (d.op == MK_OP_DOWN) {
+        if (d.a + 1 < S::NCH) {
+          sh.dpart[d.a][pr] = v;
+        } else {
+          float acc2 = 0.f;
+#pragma unroll
+          for (int c = 0; c + 1 < S::NCH; ++c) acc2 += sh.dpart[c][pr];
+          ll_store(p.ll_x + (size_t)(2 * l + 2) * S::D + gr, sh.xres[1][pr] + (acc2 + v), epoch);
+        }
+      } else {   // MK_OP_LMHEAD
+        p.logits[gr] = v;
+        const u64 key = amax_key(v, (uint32_t)gr);
+        if (key > *best) *best = key;
+      }
     }
   }
   return true;
@@ -625,14 +666,14 @@ struct AttnState {
 };
 
 template <int HD, int HPG>
-__device__ __forceinline__ void attn_init(AttnState<HD, HPG>& st, const MkShared& sh, int lane) {
+__device__ __forceinline__ void attn_init(AttnState<HD, HPG>& st, const float* act, int lane) {
   constexpr int LPP = HD / 8;
   const int c = lane % LPP;
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      st.q[h][e] = sh.act[h * HD + c * 8 + e];
+      st.q[h][e] = act[h * HD + c * 8 + e];
       st.o[h][e] = 0.f;
     }
     st.m[h] = -INFINITY;
@@ -699,366 +740,319 @@ __device__ __forceinline__ void attn_page(AttnState<HD, HPG>& st, const char* pa
 
 // Reduce the wave's state over its position groups and leave (m, l, o) in LDS.  The
 // HPG * 9 sums are independent: each swap step is applied to all of them before the
-// next, so their LDS round trips overlap instead of forming one long chain.
+// next, so their round trips overlap instead of forming one long chain.
 template <int HD, int HPG>
-__device__ __forceinline__ void attn_publish(AttnState<HD, HPG>& st, MkShared& sh, int w, int lane) {
+__device__ __forceinline__ void attn_publish(AttnState<HD, HPG>& st, float (*part)[HD + 2], int lane) {
   constexpr int LPP = HD / 8;
-  float* part = sh.act + MK_PART_OFF + w * HPG * (HD + 2);
+  constexpr int HB = HD == 64 ? HPG : 1;   // heads per batch of independent sums (registers)
 #pragma unroll
-  for (int off = LPP; off < 64; off <<= 1) {
-    float t[HPG][9];
+  for (int h0 = 0; h0 < HPG; h0 += HB) {
 #pragma unroll
-    for (int h = 0; h < HPG; ++h) {
-      t[h][8] = __shfl_xor(st.l[h], off);
+    for (int off = LPP; off < 64; off <<= 1) {
+      float t[HB][9];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[h][e] = __shfl_xor(st.o[h][e], off);
-    }
+      for (int h = 0; h < HB; ++h) {
+        t[h][8] = __shfl_xor(st.l[h0 + h], off);
 #pragma unroll
-    for (int h = 0; h < HPG; ++h) {
-      st.l[h] += t[h][8];
+        for (int e = 0; e < 8; ++e) t[h][e] = __shfl_xor(st.o[h0 + h][e], off);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.o[h][e] += t[h][e];
+      for (int h = 0; h < HB; ++h) {
+        st.l[h0 + h] += t[h][8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.o[h0 + h][e] += t[h][e];
+      }
     }
   }
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
     if (lane < LPP) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[h * (HD + 2) + 2 + lane * 8 + e] = st.o[h][e];
+      for (int e = 0; e < 8; ++e) part[h][2 + lane * 8 + e] = st.o[h][e];
     }
     if (lane == 0) {
-      part[h * (HD + 2)] = st.m[h];
-      part[h * (HD + 2) + 1] = st.l[h];
+      part[h][0] = st.m[h];
+      part[h][1] = st.l[h];
     }
   }
 }
 
-template <int HD, int HPG>
-__device__ __forceinline__ bool attn_run(const MkParams& p, MkShared& sh, const Dec& d, const StepGeo& g, int base,
-                                         int w, int lane) {
-  AttnState<HD, HPG> st;
-  attn_init<HD, HPG>(st, sh, lane);
+// Attention over this wave's pages of the split; every wave of an active split
+// publishes a partial (m = -inf, l = 0 when it had no page).
+template <class S>
+__device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
+                                         const float* act, int base, int w, int lane) {
+  AttnState<S::HD, S::HPG> st;
+  attn_init<S::HD, S::HPG>(st, act, lane);
   for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
-    const char* page = page_wait(p, sh, base + pg);
+    const char* page = page_wait<S>(p, sh, ring_base, base + pg);
     if (!page) return false;
-    const int npos = min(g.ppp, d.ce - (d.j0 + pg * g.ppp));
-    attn_page<HD, HPG>(st, page, npos, p.attn_scale, lane);
-    page_free(p, sh, base + pg, lane);
+    const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
+    attn_page<S::HD, S::HPG>(st, page, npos, p.attn_scale, lane);
+    page_free<S>(sh, base + pg, lane);
   }
-  attn_publish<HD, HPG>(st, sh, w, lane);
+  attn_publish<S::HD, S::HPG>(st, sh.part[w], lane);
   return true;
 }
 
-__device__ __forceinline__ void compute_wave(const MkParams& p, MkShared& sh, cinstr_t list, int nins,
-                                             const StepGeo& g, int w, int lane, uint32_t epoch) {
+template <class S>
+__device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh, const char* ring_base, cinstr_t list,
+                                             int nins, const StepGeo& g, int w, int lane, uint32_t epoch) {
   int base = 0;   // ring number of the instruction's first page
+  u64 best = 0;
   for (int i = 0; i < nins; ++i) {
-    const Dec d = decode(p, list[i], g);
+    const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
     if (!wait_flag(p, sh, &sh.act_seq, i + 1, false)) return;
+    // The last down chunk adds the partial sums of the earlier chunks, which any wave
+    // may have produced: wait until every wave has finished the previous instruction.
+    if (S::NCH > 1 && d.op == MK_OP_DOWN && d.a + 1 == S::NCH && !wait_all_done(p, sh, i, false)) return;
+    if (w == 0) trace_mark(p, i, 5, lane);
+    const float* act = sh.act[i % MK_NACT];
     bool ok = true;
     if (d.op == MK_OP_ATTN) {
-      // A split that is inactive at this position does nothing: in particular it must not
-      // write partials into act, which other waves may still read for the previous
-      // instruction (the leader releases inactive splits without waiting for them).
-      if (d.b >= g.s_eff) {
-      } else if (p.hd == 64) {
-        if (p.hpg == 4) ok = attn_run<64, 4>(p, sh, d, g, base, w, lane);
-        else if (p.hpg == 2) ok = attn_run<64, 2>(p, sh, d, g, base, w, lane);
-        else ok = attn_run<64, 1>(p, sh, d, g, base, w, lane);
-      } else {
-        if (p.hpg == 4) ok = attn_run<128, 4>(p, sh, d, g, base, w, lane);
-        else if (p.hpg == 2) ok = attn_run<128, 2>(p, sh, d, g, base, w, lane);
-        else ok = attn_run<128, 1>(p, sh, d, g, base, w, lane);
-      }
+      if (d.b < g.s_eff) ok = attn_run<S>(p, sh, ring_base, d, act, base, w, lane);   // inactive splits: nothing
+    } else if (d.op == MK_OP_O) {
+      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
+    } else if (d.op == MK_OP_DOWN) {
+      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
     } else {
-      u64 best = 0;
-      switch (d.upr) {
-        case 0: ok = gemv_narrow(p, sh, d, base, w, lane, epoch, &best); break;
-        case 1: ok = gemv_wide<1>(p, sh, d, base, w, lane, epoch, &best); break;
-        case 2: ok = gemv_wide<2>(p, sh, d, base, w, lane, epoch, &best); break;
-        case 4: ok = gemv_wide<4>(p, sh, d, base, w, lane, epoch, &best); break;
-        case 7: ok = gemv_wide<7>(p, sh, d, base, w, lane, epoch, &best); break;
-        default: ok = gemv_wide<8>(p, sh, d, base, w, lane, epoch, &best); break;
-      }
-      if (d.op == MK_OP_LMHEAD) {
-        best = wave_max_u64(best);
-        if (lane == 0) sh.amax[w] = best;
-      }
+      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
     }
     if (!ok) return;
+    if (d.op == MK_OP_LMHEAD) {
+      const u64 b = wave_max_u64(best);
+      if (lane == 0) sh.amax[w] = b;
+    }
     base += d.np;
     lds_fence();
     if (lane == 0) lds_store(&sh.done[w], i + 1);
-    trace_mark(p, blockIdx.x, i, 4 + w, lane);
+    if (w == 0) trace_mark(p, i, 6, lane);
   }
 }
 
 // ------------------------------------------------------------------ leader wave
-// Loads in the leader are issued in batches with no branch between them: a load under
-// a per-lane condition gets its own block, and the compiler then waits for each one
-// before the next (a full round trip per load).  Out-of-range lanes load a valid
-// address and discard the value.
-
-// Poll words [base, base + 64*NW) of src until all carry this step's epoch.  Word base + 64k + lane lands in wv[k]; words past `total` are loaded (the
-// arena is padded by MK_LL_PAD words) but not waited for.
-// The first pass loads every word; while words are missing, each lane re-polls only its
-// first missing word (one load per lane per round trip) and the wave reloads the whole
-// batch once one has arrived: re-polling whole vectors from every CU would compete with
-// the weight stream for HBM.  Reloading a word that already carries the epoch is
-// harmless: each word is written once per step, and a later load of a location never
-// returns an older value than an earlier one.
-template <int NW = MK_GATHER_MAXW>
-__device__ __forceinline__ bool poll_batch(const MkParams& p, MkShared& sh, const u64* src, int total, int base,
-                                           u64 (&wv)[NW], uint32_t epoch, int lane) {
-  const u64* q = src + base + lane;
-  const int lim = total - base - lane;      // word k is in range when 64k < lim
+// Poll NW words per lane (word k*64 + lane of src lands in wv[k]) until all carry this
+// step's epoch.  The first pass loads every word; while words are missing, each lane
+// re-polls only its first missing word (one load per lane per round trip) and the wave
+// reloads the whole batch once one has arrived: re-polling whole vectors from every CU
+// would compete with the weight stream.  A later load of a location never returns an
+// older value than an earlier one, and each word is written once per step.
+template <class S, int NW>
+__device__ __forceinline__ bool poll(const MkParams& p, MkShared<S>& sh, const u64* src, u64 (&wv)[NW],
+                                     uint32_t epoch, int lane) {
+  const u64* q = src + lane;
 #pragma unroll
   for (int k = 0; k < NW; ++k) wv[k] = ll_load(q + k * 64);
-  Waiter wt(true);
+  bool all = true;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) all = all && ll_ok(wv[k], epoch);
+  if (__ballot(!all) == 0) return true;
+  Waiter<S> wt(true);
   for (;;) {
-    bool all = true;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) all = all && (ll_ok(wv[k], epoch) || k * 64 >= lim);
-    if (__ballot(!all) == 0) return true;
-    int first_bad = -1;
-#pragma unroll
-    for (int k = NW - 1; k >= 0; --k)
-      first_bad = (k * 64 >= lim || ll_ok(wv[k], epoch)) ? first_bad : k;
     if (wt.tick(p, sh)) return false;
-    const u64 s = ll_load(q + (first_bad >= 0 ? first_bad * 64 : 0));
-    if (__ballot(first_bad >= 0 && ll_ok(s, epoch)) != 0) {
+    int first_bad = NW;
+#pragma unroll
+    for (int k = NW - 1; k >= 0; --k) first_bad = ll_ok(wv[k], epoch) ? first_bad : k;
+    const u64 s = ll_load(q + (first_bad < NW ? first_bad * 64 : 0));
+    if (__ballot(first_bad < NW && ll_ok(s, epoch)) != 0) {
 #pragma unroll
       for (int k = 0; k < NW; ++k) wv[k] = ll_load(q + k * 64);
+      all = true;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) all = all && ll_ok(wv[k], epoch);
+      if (__ballot(!all) == 0) return true;
     }
   }
 }
 
-// Gather `total` words of src into dst (LDS floats), waiting for the compute waves to
-// have finished instruction `prev_done` before the first LDS write.  The lane's sum of
-// squares of what it wrote goes to *ss when ss is not null.
-__device__ __forceinline__ bool gather(const MkParams& p, MkShared& sh, const u64* src, int total, float* dst,
-                                       int prev_done, uint32_t epoch, int lane, float* ss) {
-  bool waited = false;
-  float acc = 0.f;
-  for (int base = 0; base < total; base += 64 * MK_GATHER_MAXW) {
-    u64 wv[MK_GATHER_MAXW];
-    if (!poll_batch(p, sh, src, total, base, wv, epoch, lane)) return false;
-    if (base + 64 * MK_GATHER_MAXW >= total) trace_mark(p, blockIdx.x, prev_done, 1, lane);
-    if (!waited) {
-      if (!wait_all_done(p, sh, prev_done)) return false;
-      waited = true;
-    }
-    if (total - base >= 64 * MK_GATHER_MAXW) {   // a full batch: no per-word test
-#pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) {
-        const float v = ll_val(wv[k]);
-        dst[base + k * 64 + lane] = v;
-        acc = fmaf(v, v, acc);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) {
-        const int idx = base + k * 64 + lane;
-        if (idx < total) {
-          const float v = ll_val(wv[k]);
-          dst[idx] = v;
-          acc = fmaf(v, v, acc);
-        }
-      }
-    }
-  }
-  if (!waited && !wait_all_done(p, sh, prev_done)) return false;
-  if (ss) *ss = acc;
-  return true;
+// Wait until slot i % MK_NACT of the activation ring may be overwritten: every compute
+// wave has finished instruction i - MK_NACT.
+template <class S>
+__device__ __forceinline__ bool slot_free(const MkParams& p, MkShared<S>& sh, int i) {
+  return i < MK_NACT || wait_all_done(p, sh, i - MK_NACT + 1, true);
 }
 
 // RMSNorm staging: act = x * (1 / sqrt(mean(x^2) + eps)) * g, with x the residual
 // stream (the embedding row for the first layer).  Rows [res_r0, res_r0 + res_n) of the
-// raw x are kept for the residual add of the next O / DOWN instruction.  The gains go
-// to LDS before any wait.  Vectors of up to 64 * MK_GATHER_MAXW values stay in
-// registers between the sum of squares and the scaled write (one LDS pass); longer ones
-// are normalised in place in a second pass.
-__device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared& sh, const u64* src, const uint16_t* gain,
-                                           int res_r0, int res_n, int i, uint32_t epoch, int lane) {
-  const int d = p.d, npair = d >> 1;
-  for (int b0 = 0; b0 < npair; b0 += 64 * 16) {   // gain pairs, 16 loads per lane per batch
-    uint32_t gp[16];
+// raw x are kept for the residual add of the next O / DOWN instruction (xres[which]).
+// Up to 2048 values stay in registers between the sum of squares and the scaled write;
+// longer vectors are written raw in batches and normalised in place.
+template <class S>
+__device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, const u64* src, const uint16_t* gain,
+                                           int res_r0, int res_n, int which, int i, uint32_t epoch, int lane) {
+  constexpr int NW = S::D / 64;
+  constexpr int BW = NW < 32 ? NW : 32;   // words per lane per batch
+  constexpr int NG = S::D / 128;          // gain pairs per lane: lane holds pairs lane + 64k
+  uint32_t gp[NG];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) gp[k] = ((const uint32_t*)gain)[min(b0 + k * 64 + lane, npair - 1)];
+  for (int k = 0; k < NG; ++k) gp[k] = ((const uint32_t*)gain)[k * 64 + lane];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) pin(gp[k]);
-#pragma unroll
-    for (int k = 0; k < 16; ++k)   // lanes past the end rewrite the last pair with its own value
-      ((uint32_t*)sh.gain)[min(b0 + k * 64 + lane, npair - 1)] = gp[k];
-  }
-  if (d <= 64 * MK_GATHER_MAXW) {
-    const int kmax = d >> 6;   // hidden is a multiple of 64: word k is in range iff k < kmax
-    float xv[MK_GATHER_MAXW];
+  for (int k = 0; k < NG; ++k) pin(gp[k]);
+  // Element k*64 + lane is half (lane & 1) of gain pair 32k + lane/2, which sits in
+  // lane (lane/2 + 32k) % 64 = lane/2 + 32 (k & 1), register gp[k / 2].
+  auto gain_of = [&](int k) {
+    const uint32_t pair = __shfl(gp[k >> 1], (lane >> 1) + 32 * (k & 1));
+    return (lane & 1) ? bf_hi(pair) : bf_lo(pair);
+  };
+  trace_mark(p, i, 1, lane);
+  float* act = sh.act[i % MK_NACT];
+  float ss = 0.f;
+  float xv[BW];
+  for (int b = 0; b < NW; b += BW) {
     if (src == nullptr) {
-      const uint16_t* e = p.embed + (size_t)sh.token * d;
-      uint32_t eb[MK_GATHER_MAXW];
+      const uint16_t* e = p.embed + (size_t)sh.token * S::D + b * 64;
+      uint32_t eb[BW];
 #pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) eb[k] = e[min(k * 64 + lane, d - 1)];
+      for (int k = 0; k < BW; ++k) eb[k] = e[k * 64 + lane];
 #pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) pin(eb[k]);
+      for (int k = 0; k < BW; ++k) pin(eb[k]);
 #pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) xv[k] = k * 64 + lane < d ? bf16f((uint16_t)eb[k]) : 0.f;
+      for (int k = 0; k < BW; ++k) xv[k] = bf16f((uint16_t)eb[k]);
     } else {
-      u64 wv[MK_GATHER_MAXW];
-      if (!poll_batch(p, sh, src, d, 0, wv, epoch, lane)) return false;
-      trace_mark(p, blockIdx.x, i, 1, lane);
+      u64 wv[BW];
+      if (!poll<S, BW>(p, sh, src + b * 64, wv, epoch, lane)) return false;
 #pragma unroll
-      for (int k = 0; k < MK_GATHER_MAXW; ++k) xv[k] = k < kmax ? ll_val(wv[k]) : 0.f;
+      for (int k = 0; k < BW; ++k) xv[k] = ll_val(wv[k]);
     }
-    float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) ss = fmaf(xv[k], xv[k], ss);
-    const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + p.eps);
-    // All LDS reads first, then all writes: a read issued after a write waits for it.
-    uint32_t gl[MK_GATHER_MAXW];
+    for (int k = 0; k < BW; ++k) ss = fmaf(xv[k], xv[k], ss);
+    if constexpr (NW > BW) {   // raw batch into the slot; normalised below
+      if (b == 0 && !slot_free(p, sh, i)) return false;
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) gl[k] = sh.gain[(k < kmax ? k * 64 : 0) + lane];
+      for (int k = 0; k < BW; ++k) act[(b + k) * 64 + lane] = xv[k];
+    }
+  }
+  trace_mark(p, i, 2, lane);
+  const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)S::D + p.eps);
+  if constexpr (NW > BW) {
+    lds_fence();
+    const float r = lane < res_n ? act[res_r0 + lane] : 0.f;
+    trace_mark(p, i, 3, lane);
+    if (lane < res_n) sh.xres[which][lane] = r;
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) pin(gl[k]);
-    float nv[MK_GATHER_MAXW];
+    for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (act[k * 64 + lane] * rinv) * gain_of(k);
+  } else {
+    float nv[NW];
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) nv[k] = (xv[k] * rinv) * bf16f((uint16_t)gl[k]);
-    // Residual rows res_r0 + j (j < res_n <= 64) lie in words k0 and k0 + 1: pick those two
-    // words with uniform selects, then fetch each row's value from the lane that holds it.
+    for (int k = 0; k < NW; ++k) nv[k] = (xv[k] * rinv) * gain_of(k);
+    // Residual rows res_r0 + j (j < res_n <= 64) lie in words k0 and k0 + 1.
     const int k0 = res_r0 >> 6;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k) {
+    for (int k = 0; k < NW; ++k) {
       a0 = k == k0 ? xv[k] : a0;
       a1 = k == k0 + 1 ? xv[k] : a1;
     }
     const int ridx = res_r0 + lane;
     const float b0 = __shfl(a0, ridx & 63), b1 = __shfl(a1, ridx & 63);
-    if (!wait_all_done(p, sh, i)) return false;
+    if (!slot_free(p, sh, i)) return false;
+    trace_mark(p, i, 3, lane);
 #pragma unroll
-    for (int k = 0; k < MK_GATHER_MAXW; ++k)
-      if (k < kmax) sh.act[k * 64 + lane] = nv[k];
-    if (lane < res_n) sh.xres[lane] = (ridx >> 6) == k0 ? b0 : b1;
-    return true;
+    for (int k = 0; k < NW; ++k) act[k * 64 + lane] = nv[k];
+    if (lane < res_n) sh.xres[which][lane] = (ridx >> 6) == k0 ? b0 : b1;
   }
-  float ss = 0.f;
-  if (src == nullptr) {
-    const uint16_t* e = p.embed + (size_t)sh.token * d;
-    if (!wait_all_done(p, sh, i)) return false;
-    for (int b0 = 0; b0 < d; b0 += 64 * 16) {
-      uint32_t eb[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) eb[k] = e[min(b0 + k * 64 + lane, d - 1)];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) pin(eb[k]);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int idx = b0 + k * 64 + lane;
-        const float v = idx < d ? bf16f((uint16_t)eb[k]) : 0.f;
-        if (idx < d) sh.act[idx] = v;
-        ss = fmaf(v, v, ss);
-      }
-    }
-  } else {
-    if (!gather(p, sh, src, d, sh.act, i, epoch, lane, &ss)) return false;
-  }
-  const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + p.eps);
-  lds_fence();
-  for (int j = lane; j < res_n; j += 64) sh.xres[j] = sh.act[res_r0 + j];
-  for (int idx = lane; idx < d; idx += 64) sh.act[idx] = (sh.act[idx] * rinv) * bf16f(sh.gain[idx]);
   return true;
 }
 
-__device__ __forceinline__ bool stage_raw(const MkParams& p, MkShared& sh, const u64* src, int n, int i,
-                                          uint32_t epoch, int lane) {
-  return gather(p, sh, src, n, sh.act, i, epoch, lane, nullptr);
+template <class S, int N>
+__device__ __forceinline__ bool stage_raw(const MkParams& p, MkShared<S>& sh, const u64* src, int i, uint32_t epoch,
+                                          int lane) {
+  constexpr int NW = N / 64;
+  u64 wv[NW];
+  trace_mark(p, i, 1, lane);
+  if (!poll<S, NW>(p, sh, src, wv, epoch, lane)) return false;
+  trace_mark(p, i, 2, lane);
+  if (!slot_free(p, sh, i)) return false;
+  trace_mark(p, i, 3, lane);
+  float* act = sh.act[i % MK_NACT];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) act[k * 64 + lane] = ll_val(wv[k]);
+  return true;
 }
 
 // Attention staging for item (kv head g, split s): q of the group's heads, the new k
 // and v; RoPE on q and k; k, v rounded to bf16 (what the cache holds).  The split that
-// contains the current position writes k, v into cache slot pos.  Everything happens in
-// registers between the poll and one batch of LDS writes.  Word idx = 64j + lane of the
-// group holds element e = idx % hd of head idx / hd; its rotation partner e +- hd/2 is
-// in lane ^ 32 of the same word (hd 64) or in the same lane of word j ^ 1 (hd 128).
-constexpr int MK_ATTN_NW = 12;   // (4 + 2) heads x 128 / 64: words per lane of the largest group
-__device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared& sh, const MkInstr& in, const StepGeo& g,
+// contains the current position writes k, v into cache slot pos.  Word j of the group
+// (elements 64j + lane) lies in one head; element e's rotation partner e +- hd/2 is in
+// lane ^ 32 of the same word (hd 64) or the same lane of word j ^ 1 (hd 128).
+template <class S>
+__device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, const MkInstr& in, const StepGeo& g,
                                            int i, uint32_t epoch, int lane) {
-  const int hd = p.hd, hpg = p.hpg, half = hd >> 1, l = in.layer, gi = in.a;
-  const int total = (hpg + 2) * hd;
-  const u64* src = p.ll_qkv + (size_t)l * p.nqkv + (size_t)gi * total;   // group-major q | k | v
-  const float* cs = p.rope + (size_t)g.pos * hd + 2 * (lane & (half - 1));  // [half][2], e % half == lane % half
+  constexpr int HD = S::HD, HALF = HD / 2, NW = S::GRP / 64;
+  constexpr int KB = S::HPG * HD, VB = (S::HPG + 1) * HD;   // offsets of k and v in the group
+  const int l = in.layer, gi = in.a;
+  const u64* src = p.ll_qkv + (size_t)l * S::NQKV + (size_t)gi * S::GRP;
+  const float* cs = p.rope + (size_t)g.pos * HD + 2 * (lane & (HALF - 1));   // [half][2]
   const float c = cs[0], sn = cs[1];
-  u64 wv[MK_ATTN_NW];
-  if (!poll_batch<MK_ATTN_NW>(p, sh, src, total, 0, wv, epoch, lane)) return false;
-  trace_mark(p, blockIdx.x, i, 1, lane);
-  float v[MK_ATTN_NW];
+  u64 wv[NW];
+  trace_mark(p, i, 1, lane);
+  if (!poll<S, NW>(p, sh, src, wv, epoch, lane)) return false;
+  trace_mark(p, i, 2, lane);
+  float v[NW];
 #pragma unroll
-  for (int j = 0; j < MK_ATTN_NW; ++j) v[j] = ll_val(wv[j]);
-  float pr[MK_ATTN_NW];   // rotation partners
-  const bool hd64 = hd == 64;
+  for (int j = 0; j < NW; ++j) v[j] = ll_val(wv[j]);
+  float pr[NW];   // rotation partners
 #pragma unroll
-  for (int j = 0; j < MK_ATTN_NW; ++j) {
-    const float x = __shfl_xor(v[j], 32);
-    pr[j] = hd64 ? x : v[j ^ 1];
-  }
-  const int kbase = hpg * hd, vbase = (hpg + 1) * hd;   // offsets of k and v in the group
+  for (int j = 0; j < NW; ++j) pr[j] = HD == 64 ? __shfl_xor(v[j], 32) : v[j ^ 1];
   const bool has_pos = in.b == g.s_eff - 1;
-  uint16_t* kslot = p.kv + ((((size_t)l * 2) * p.hkv + gi) * p.max_ctx + g.pos) * hd;
-  uint16_t* vslot = kslot + (size_t)p.hkv * p.max_ctx * hd;
+  uint16_t* kslot = p.kv + ((((size_t)l * 2) * S::HKV + gi) * p.max_ctx + g.pos) * HD;
+  uint16_t* vslot = kslot + (size_t)S::HKV * p.max_ctx * HD;
 #pragma unroll
-  for (int j = 0; j < MK_ATTN_NW; ++j) {
+  for (int j = 0; j < NW; ++j) {
     const int idx = j * 64 + lane;
-    const bool first = hd64 ? lane < 32 : (j & 1) == 0;   // e < half
-    if (idx < vbase) {   // q heads and k: rotate
+    const bool first = HD == 64 ? lane < 32 : (j & 1) == 0;   // e < half
+    if (j * 64 < VB) {   // q heads and k: rotate
       v[j] = first ? __fsub_rn(__fmul_rn(v[j], c), __fmul_rn(pr[j], sn))
                    : __fadd_rn(__fmul_rn(v[j], c), __fmul_rn(pr[j], sn));
     }
-    if (idx >= kbase && idx < total) {   // k and v: what the cache holds
+    if (j * 64 >= KB) {   // k and v: what the cache holds
       const uint16_t b = f2bf(v[j]);
       v[j] = bf16f(b);
-      if (has_pos) (idx < vbase ? kslot : vslot)[idx - (idx < vbase ? kbase : vbase)] = b;
+      if (has_pos) (idx < VB ? kslot : vslot)[idx - (idx < VB ? KB : VB)] = b;
     }
   }
-  if (!wait_all_done(p, sh, i)) return false;
+  if (!slot_free(p, sh, i)) return false;
+  trace_mark(p, i, 3, lane);
+  float* act = sh.act[i % MK_NACT];
 #pragma unroll
-  for (int j = 0; j < MK_ATTN_NW; ++j)
-    if (j * 64 + lane < total) sh.act[j * 64 + lane] = v[j];
+  for (int j = 0; j < NW; ++j) act[j * 64 + lane] = v[j];
   return true;
 }
 
+template <class S>
 __device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, int h, int s) {
-  return ((((size_t)l * p.hkv + g) * p.hpg + h) * p.s_max + s) * (size_t)(p.hd + 2);
+  return ((((size_t)l * S::HKV + g) * S::HPG + h) * p.s_max + s) * (size_t)(S::HD + 2);
 }
 
 // After the compute waves: combine their partials (and the current position's key)
 // into this split's (m, l, o), then either write o (single split), publish the split,
 // and/or merge all splits of one head (CUs with split index < heads per group).  Lane
-// `lane` handles elements lane + 64c of each head.  LDS reads are batched ahead of use.
-template <int HD, int HPG>
-__device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared& sh, const MkInstr& in, const StepGeo& g,
-                                              int i, uint32_t epoch, int lane) {
-  constexpr int E = HD / 64, STRIDE = HD + 2;
+// `lane` handles elements lane + 64c of each head.
+template <class S>
+__device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh, const MkInstr& in,
+                                              const StepGeo& g, int i, uint32_t epoch, int lane) {
+  constexpr int HD = S::HD, HPG = S::HPG, E = HD / 64, STRIDE = HD + 2;
   const int l = in.layer, gi = in.a, s = in.b;
+  const float* act = sh.act[i % MK_NACT];
   if (s < g.s_eff) {
     const bool has_pos = s == g.s_eff - 1;
-    const float* part = sh.act + MK_PART_OFF;
     float mw[MK_NC][HPG], lw[MK_NC][HPG], ow[MK_NC][HPG][E], qv[HPG][E], kn[E], vn[E];
 #pragma unroll
     for (int w = 0; w < MK_NC; ++w)
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
-        mw[w][h] = part[(w * HPG + h) * STRIDE];
-        lw[w][h] = part[(w * HPG + h) * STRIDE + 1];
+        mw[w][h] = sh.part[w][h][0];
+        lw[w][h] = sh.part[w][h][1];
 #pragma unroll
-        for (int c = 0; c < E; ++c) ow[w][h][c] = part[(w * HPG + h) * STRIDE + 2 + c * 64 + lane];
+        for (int c = 0; c < E; ++c) ow[w][h][c] = sh.part[w][h][2 + c * 64 + lane];
       }
 #pragma unroll
     for (int c = 0; c < E; ++c) {
 #pragma unroll
-      for (int h = 0; h < HPG; ++h) qv[h][c] = sh.act[h * HD + c * 64 + lane];
-      kn[c] = sh.act[HPG * HD + c * 64 + lane];
-      vn[c] = sh.act[(HPG + 1) * HD + c * 64 + lane];
+      for (int h = 0; h < HPG; ++h) qv[h][c] = act[h * HD + c * 64 + lane];
+      kn[c] = act[HPG * HD + c * 64 + lane];
+      vn[c] = act[(HPG + 1) * HD + c * 64 + lane];
     }
     float sp[HPG];   // score of the current position (the key that is not in the cache yet)
 #pragma unroll
@@ -1090,46 +1084,71 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared& sh, c
         for (int w = 0; w < MK_NC; ++w) o = fmaf(ow[w][h][c], wt[w], o);
         const int e = c * 64 + lane;
         if (g.s_eff == 1)
-          ll_store(p.ll_o + (size_t)l * p.nq + (gi * HPG + h) * HD + e, o / L, epoch);
+          ll_store(p.ll_o + (size_t)l * S::NQ + (gi * HPG + h) * HD + e, o / L, epoch);
         else
-          ll_store(p.ll_part + part_index(p, l, gi, h, s) + 2 + e, o, epoch);
+          ll_store(p.ll_part + part_index<S>(p, l, gi, h, s) + 2 + e, o, epoch);
       }
       if (g.s_eff > 1 && lane == 0) {
-        ll_store(p.ll_part + part_index(p, l, gi, h, s), M, epoch);
-        ll_store(p.ll_part + part_index(p, l, gi, h, s) + 1, L, epoch);
+        ll_store(p.ll_part + part_index<S>(p, l, gi, h, s), M, epoch);
+        ll_store(p.ll_part + part_index<S>(p, l, gi, h, s) + 1, L, epoch);
       }
     }
   }
   if (g.s_eff > 1 && s < HPG) {
-    // Merge head s of this group over all splits.
+    // Merge head s of this group over all splits; split t's words are [t*STRIDE, +STRIDE):
+    // (m, l, o[HD]).  Splits are polled MB at a time and folded in split order.
     const int h = s;
-    lds_fence();
-    if (!gather(p, sh, p.ll_part + part_index(p, l, gi, h, 0), g.s_eff * STRIDE, sh.act, i + 1, epoch, lane,
-                nullptr))
-      return false;
-    lds_fence();
-    float M = -INFINITY;
-    for (int t = 0; t < g.s_eff; ++t) M = fmaxf(M, sh.act[t * STRIDE]);
-    float L = 0.f, o[E];
+    const u64* src = p.ll_part + part_index<S>(p, l, gi, h, 0);
+    float M = -INFINITY, L = 0.f, o[E];
 #pragma unroll
     for (int c = 0; c < E; ++c) o[c] = 0.f;
-    for (int t = 0; t < g.s_eff; ++t) {
-      const float mt = sh.act[t * STRIDE];
-      const float wt = mt == -INFINITY ? 0.f : __expf(mt - M);
-      L = fmaf(sh.act[t * STRIDE + 1], wt, L);
+    Waiter<S> wt(true);
+    constexpr int MB = 16 / E;
+    for (int t0 = 0; t0 < g.s_eff; t0 += MB) {
+      u64 ml, ow[MB][E];
+      const int tl = t0 + (lane & 15);
+      for (;;) {
+        // lanes 0-15: m of split t0 + lane; lanes 16-31: its l (lanes 32-63 repeat them)
+        ml = ll_load(src + (size_t)(tl < g.s_eff ? tl : t0) * STRIDE + ((lane >> 4) & 1));
 #pragma unroll
-      for (int c = 0; c < E; ++c) o[c] = fmaf(sh.act[t * STRIDE + 2 + c * 64 + lane], wt, o[c]);
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int c = 0; c < E; ++c)
+            ow[j][c] = ll_load(src + (size_t)(t0 + j < g.s_eff ? t0 + j : t0) * STRIDE + 2 + c * 64 + lane);
+        bool ok = ll_ok(ml, epoch);
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int c = 0; c < E; ++c) ok = ok && ll_ok(ow[j][c], epoch);
+        if (__ballot(!ok) == 0) break;
+        if (wt.tick(p, sh)) return false;
+      }
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const float mt = __shfl(ll_val(ml), j), lt = __shfl(ll_val(ml), 16 + j);
+        if (t0 + j < g.s_eff) {
+          const float Mn = fmaxf(M, mt);
+          const float a = M == -INFINITY ? 0.f : __expf(M - Mn);
+          const float b = mt == -INFINITY ? 0.f : __expf(mt - Mn);
+          L = L * a + lt * b;
+#pragma unroll
+          for (int c = 0; c < E; ++c) o[c] = o[c] * a + ll_val(ow[j][c]) * b;
+          M = Mn;
+        }
+      }
     }
 #pragma unroll
     for (int c = 0; c < E; ++c)
-      ll_store(p.ll_o + (size_t)l * p.nq + (gi * HPG + h) * HD + c * 64 + lane, o[c] / L, epoch);
+      ll_store(p.ll_o + (size_t)l * S::NQ + (gi * HPG + h) * HD + c * 64 + lane, o[c] / L, epoch);
   }
   return true;
 }
 
 // Final argmax: combine the waves, publish the CU's key, take a ticket; the last CU
 // reduces all keys, writes the next token and advances the epoch for the next step.
-__device__ __forceinline__ void lm_finalize(const MkParams& p, MkShared& sh, uint32_t epoch, int cu, int lane) {
+template <class S>
+__device__ __forceinline__ void lm_finalize(const MkParams& p, MkShared<S>& sh, uint32_t epoch, int lane) {
+  const int cu = blockIdx.x;
   u64 key = 0;
   for (int w = 0; w < MK_NC; ++w) key = sh.amax[w] > key ? sh.amax[w] : key;
   uint32_t old = 0;
@@ -1157,68 +1176,61 @@ __device__ __forceinline__ void lm_finalize(const MkParams& p, MkShared& sh, uin
   }
 }
 
-__device__ __forceinline__ void leader_wave(const MkParams& p, MkShared& sh, cinstr_t list, int nins, const StepGeo& g,
-                            int lane, uint32_t epoch, int cu) {
+template <class S>
+__device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, cinstr_t list, int nins,
+                                            const StepGeo& g, int lane, uint32_t epoch) {
   for (int i = 0; i < nins; ++i) {
     const MkInstr in = list[i];
     const int l = in.layer;
     lane = opaque(lane);
-    trace_mark(p, cu, i, 0, lane);
+    trace_mark(p, i, 0, lane);
     bool ok = true;
     switch (in.op) {
       case MK_OP_QKV:
-        ok = stage_norm(p, sh, l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * p.d, ((clayers_t)p.layers)[l].attn_norm,
-                        in.res_r0, in.res_n, i, epoch, lane);
+        ok = stage_norm<S>(p, sh, l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D,
+                           ((clayers_t)p.layers)[l].attn_norm, in.res_r0, in.res_n, 0, i, epoch, lane);
         break;
       case MK_OP_ATTN:
-        if (in.b < g.s_eff) ok = stage_attn(p, sh, in, g, i, epoch, lane);
+        if (in.b < g.s_eff) ok = stage_attn<S>(p, sh, in, g, i, epoch, lane);
         break;
       case MK_OP_O:
-        ok = stage_raw(p, sh, p.ll_o + (size_t)l * p.nq, p.nq, i, epoch, lane);
+        ok = stage_raw<S, S::NQ>(p, sh, p.ll_o + (size_t)l * S::NQ, i, epoch, lane);
         break;
       case MK_OP_GATEUP:
-        ok = stage_norm(p, sh, p.ll_x + (size_t)(2 * l + 1) * p.d, ((clayers_t)p.layers)[l].mlp_norm, in.res_r0, in.res_n, i,
-                        epoch, lane);
+        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l + 1) * S::D, ((clayers_t)p.layers)[l].mlp_norm,
+                           in.res_r0, in.res_n, 1, i, epoch, lane);
         break;
       case MK_OP_DOWN:
-        ok = stage_raw(p, sh, p.ll_a + (size_t)l * p.F + in.k0, in.kn, i, epoch, lane);
+        ok = stage_raw<S, S::KC>(p, sh, p.ll_a + (size_t)l * S::F + in.k0, i, epoch, lane);
         break;
       default:  // MK_OP_LMHEAD (its record carries layer = n_layers: the last residual version)
-        ok = stage_norm(p, sh, p.ll_x + (size_t)(2 * l) * p.d, ((clayers_t)p.layers)[l].attn_norm, 0, 0, i,
-                        epoch, lane);
+        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l) * S::D, ((clayers_t)p.layers)[l].attn_norm, 0, 0, 0,
+                           i, epoch, lane);
         break;
     }
     if (!ok) return;
     lds_fence();
     if (lane == 0) lds_store(&sh.act_seq, i + 1);
-    trace_mark(p, cu, i, 2, lane);
+    trace_mark(p, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
-      if (!wait_all_done(p, sh, i + 1)) return;
-      bool fin;
-      if (p.hd == 64) {
-        fin = p.hpg == 4 ? attn_finalize<64, 4>(p, sh, in, g, i, epoch, lane)
-            : p.hpg == 2 ? attn_finalize<64, 2>(p, sh, in, g, i, epoch, lane)
-                         : attn_finalize<64, 1>(p, sh, in, g, i, epoch, lane);
-      } else {
-        fin = p.hpg == 4 ? attn_finalize<128, 4>(p, sh, in, g, i, epoch, lane)
-            : p.hpg == 2 ? attn_finalize<128, 2>(p, sh, in, g, i, epoch, lane)
-                         : attn_finalize<128, 1>(p, sh, in, g, i, epoch, lane);
-      }
-      if (!fin) return;
+      if (!wait_all_done(p, sh, i + 1, true)) return;
+      if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
     } else if (in.op == MK_OP_LMHEAD) {
-      if (!wait_all_done(p, sh, i + 1)) return;
-      lm_finalize(p, sh, epoch, cu, lane);
+      if (!wait_all_done(p, sh, i + 1, true)) return;
+      lm_finalize<S>(p, sh, epoch, lane);
     }
-    trace_mark(p, cu, i, 3, lane);
+    trace_mark(p, i, 7, lane);
   }
 }
 
 }  // namespace mkdev
 
 // One decode step.  Grid: one work-group per CU (all resident: cooperative launch).
+template <class S>
 __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   using namespace mkdev;
-  __shared__ MkShared sh;
+  __shared__ MkShared<S> sh;
+  __shared__ __align__(16) char ring[Ring<S>::NSLOT * MK_PAGE_BYTES];
   // the wave index is uniform per wave; saying so keeps everything derived from it scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, cu = blockIdx.x;
   if (threadIdx.x == 0) {
@@ -1245,8 +1257,8 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   const int o0 = ((cint_t)p.plan_off)[cu];
   const int nins = ((cint_t)p.plan_off)[cu + 1] - o0;
   cinstr_t list = (cinstr_t)p.plan + o0;
-  const StepGeo g = step_geo(p, p.pos);
-  if (wave < MK_NC) compute_wave(p, sh, list, nins, g, wave, lane, epoch);
-  else if (wave < MK_NC + MK_NL) loader_wave(p, sh, list, nins, g, wave - MK_NC, lane);
-  else leader_wave(p, sh, list, nins, g, lane, epoch, cu);
+  const StepGeo g = step_geo<S>(p, p.pos);
+  if (wave < MK_NC) compute_wave<S>(p, sh, ring, list, nins, g, wave, lane, epoch);
+  else if (wave < MK_NC + MK_NL) loader_wave<S>(p, sh, ring, list, nins, g, wave - MK_NC, lane);
+  else leader_wave<S>(p, sh, list, nins, g, lane, epoch);
 }

@@ -16,32 +16,9 @@
 
 #include <algorithm>
 
+#include "mk_shapes.h"
+
 namespace {
-
-bool seg_ok(int k_elems) {
-  long bytes = 2L * k_elems;
-  if (bytes <= 0) return false;
-  if (bytes < 1024) return bytes >= 256 && (bytes & (bytes - 1)) == 0;   // <= 64 rows per page
-  return bytes % 1024 == 0;
-}
-
-int down_chunks(const mk_config& c) {
-  // The article splits the MLP intermediate into 4 chunks so the down projection
-  // can start on a chunk as soon as it is written.
-  for (int nch : {4, 2, 1})
-    if (c.ffn % nch == 0 && seg_ok(c.ffn / nch) && c.ffn / nch <= MK_ACT_FLOATS) return nch;
-  return 0;
-}
-
-int pick_page_bytes(const mk_config& c, int nch) {
-  long need = std::max<long>({4L * c.hidden,                   // a gate row and its up row
-                              2L * c.n_q_heads * c.head_dim,   // one O row
-                              2L * (c.ffn / std::max(nch, 1)), // one DOWN chunk row
-                              4L * c.head_dim});               // one key and its value
-  for (int pb : {8192, 16384})
-    if (need <= pb) return pb;
-  return 0;
-}
 
 void split(int n, int parts, int i, int* r0, int* cnt) {
   long a = (long)n * i / parts, b = (long)n * (i + 1) / parts;
@@ -58,33 +35,39 @@ MkInstr mk(int op, int layer) {
 
 }  // namespace
 
-int mk_check_config(const mk_config& c, std::string* why) {
-  auto bad = [&](const char* m) {
+int mk_check_config(const mk_config& c, std::string* why, int* nch) {
+  auto bad = [&](const std::string& m) {
     if (why) *why = m;
     return MK_EINVAL;
   };
   if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.ffn < 1 ||
       c.vocab < 1 || c.max_ctx < 1)
     return bad("every dimension must be positive");
-  if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
-  if (c.n_q_heads % c.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
-  int hpg = c.n_q_heads / c.n_kv_heads;
-  if (hpg != 1 && hpg != 2 && hpg != 4) return bad("query heads per KV head must be 1, 2 or 4");
-  if ((hpg + 2) * c.head_dim > MK_PART_OFF) return bad("(q heads per group + 2) * head_dim exceeds 1024");
-  if (MK_NC * hpg * (c.head_dim + 2) > MK_ACT_FLOATS - MK_PART_OFF) return bad("attention partials exceed LDS");
-  if (c.hidden > MK_ACT_FLOATS || c.n_q_heads * c.head_dim > MK_ACT_FLOATS)
-    return bad("hidden and n_q_heads*head_dim must be <= 4096");
-  if (!seg_ok(c.hidden) || !seg_ok(c.n_q_heads * c.head_dim))
-    return bad("hidden and n_q_heads*head_dim must be 128, 256 or a multiple of 512");
-  int nch = down_chunks(c);
-  if (!nch) return bad("ffn/4 (or ffn/2, ffn) must be 128, 256 or a multiple of 512, and <= 4096");
-  if (!pick_page_bytes(c, nch)) return bad("rows too long for a 16 KiB page");
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0f)) return bad("rms_eps must be >= 0 and rope_theta > 0");
+  int found = 0;
+#define MK_MATCH(D, HQ, HKV, HD, F, NCH) \
+  if (!found && c.hidden == D && c.n_q_heads == HQ && c.n_kv_heads == HKV && c.head_dim == HD && c.ffn == F) found = NCH;
+  MK_SHAPES(MK_MATCH)
+#undef MK_MATCH
+  if (!found) {
+    std::string m = "unsupported shape (hidden, n_q_heads, n_kv_heads, head_dim, ffn) = (" +
+                    std::to_string(c.hidden) + ", " + std::to_string(c.n_q_heads) + ", " +
+                    std::to_string(c.n_kv_heads) + ", " + std::to_string(c.head_dim) + ", " +
+                    std::to_string(c.ffn) + "); compiled:";
+#define MK_LIST(D, HQ, HKV, HD, F, NCH) \
+  m += " (" + std::to_string(D) + ", " + std::to_string(HQ) + ", " + std::to_string(HKV) + ", " + \
+       std::to_string(HD) + ", " + std::to_string(F) + ")";
+    MK_SHAPES(MK_LIST)
+#undef MK_LIST
+    return bad(m);
+  }
+  if (nch) *nch = found;
   return MK_OK;
 }
 
 int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) {
-  int rc = mk_check_config(c, why);
+  int nch = 0;
+  int rc = mk_check_config(c, why, &nch);
   if (rc) return rc;
   if (n_cus < 1) {
     if (why) *why = "n_cus must be positive";
@@ -94,16 +77,12 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
     if (why) *why = "hidden / n_cus exceeds the 64 residual rows one CU may own";
     return MK_EINVAL;
   }
-  const int nch = down_chunks(c);
   MkPlan p;
   p.n_cus = n_cus;
-  p.page_bytes = pick_page_bytes(c, nch);
-  p.slots = MK_PAGES_BYTES / p.page_bytes;
-  if (2 * c.hidden * 2 > p.page_bytes || p.page_bytes / (4 * c.hidden) > MK_GATE_SCRATCH) {
-    if (why) *why = "gate/up page geometry unsupported";
-    return MK_EINVAL;
-  }
-  p.s_max = std::max(1, std::min(n_cus / c.n_kv_heads, MK_ACT_FLOATS / (c.head_dim + 2)));
+  p.nch = nch;
+  p.page_bytes = MK_PAGE_BYTES;
+  // The merge of one head's splits polls 16 splits per round; 32 keeps it to two rounds.
+  p.s_max = std::max(1, std::min(n_cus / c.n_kv_heads, 32));
   p.min_chunk = 256;
   if (p.s_max < c.n_q_heads / c.n_kv_heads) {
     if (why) *why = "too few CUs for one merger per query head of a group";

@@ -9,24 +9,16 @@
 
 // Work-group shape, one work-group per CU: MK_NC compute waves that only read LDS,
 // MK_NL loader waves that only stream pages HBM -> LDS, and one leader wave that
-// waits on dependencies and stages the activation vector.
+// waits on dependencies and stages activation vectors.
 #define MK_NC 4
 #define MK_NL 2
 #define MK_NWAVES (MK_NC + MK_NL + 1)
 #define MK_THREADS (64 * MK_NWAVES)
-#define MK_MAX_SLOTS 32
-
-// LDS budget (gfx950 has 160 KiB per work-group).
-#define MK_ACT_FLOATS 4096                // activation vector staged per instruction
-#define MK_PAGES_BYTES (128 * 1024)       // page ring shared by the loaders and compute waves
+#define MK_MAX_SLOTS 16
+#define MK_PAGE_BYTES 16384               // one LDS page: 16 units of 1 KiB
+#define MK_NACT 2                         // staged activation vectors (ring)
 #define MK_MAX_RES_ROWS 64                // rows of x one CU owns in a residual op
-#define MK_GATE_SCRATCH 16                // gate results held per wave until the up row
-#define MK_MAX_HPG 8                      // query heads per KV head
-#define MK_PART_OFF 1024                  // offset (floats) of per-wave attention partials in act
-#define MK_GATHER_MAXW 32                 // words per lane one gather batch holds
-// The activation-word arena is padded by one gather batch, so a batch may load past the
-// end of the vector it polls without a bounds test per word.
-#define MK_LL_PAD (64 * MK_GATHER_MAXW)
+#define MK_MAX_NCH 4                      // K-chunks of the down projection
 
 // Instruction opcodes — the article's six fused instructions.
 enum {
@@ -63,18 +55,15 @@ struct MkCtrl {
   uint32_t pad[4];
 };
 
-// Kernel argument block (passed by value).
+// Kernel argument block (passed by value).  The model's widths are template
+// parameters of the kernel; only what varies per call or per model depth is here.
 struct MkParams {
-  // shape
-  int32_t n_layers, d, hq, hkv, hd, F, V, max_ctx;
-  int32_t nq, nkv, nqkv, hpg;
+  int32_t n_layers, V, max_ctx, n_cus;
+  int32_t nslot, s_max, min_chunk;   // nslot: pages in the LDS ring
   float eps, attn_scale;
-  // schedule
-  int32_t n_cus, page_bytes, nslot, lpp, s_max, min_chunk;   // nslot: pages in the LDS ring
   // weights (bf16)
   const uint16_t* embed;
   const uint16_t* lm_head;
-  const uint16_t* final_norm;
   const MkLayerPtrs* layers;      // [n_layers + 1]; entry n_layers: attn_norm = final norm
   const float* rope;              // [max_ctx][hd/2][2]: cos, sin
   // static plan
@@ -100,6 +89,7 @@ struct MkParams {
   int32_t trace_len;
 };
 
-// Trace slots per instruction: leader start, inputs ready, activation staged, leader
-// done (after attention merge / argmax), then the finish time of each compute wave.
+// Trace slots per instruction: [0] leader starts, [1] leader starts polling its
+// inputs, [2] inputs all present, [3] slot free, [4] activation staged, [5] compute
+// wave 0 starts, [6] compute wave 0 done, [7] leader done (attention merge / argmax).
 #define MK_TRACE_SLOTS 8
