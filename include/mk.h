@@ -147,12 +147,16 @@ int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out);
 int mk_debug_dump(const mk_ctx* ctx, uint64_t* host, int64_t capacity_words, int64_t offsets[6]);
 
 /* Per-instruction timestamp trace (the time breakdown of one forward).  dev_buf is a
- * borrowed device buffer of uint64 [n_cus][L][8] with L the longest per-CU instruction
- * list; *required_words receives n_cus * L * 8 (pass dev_buf NULL to query, which also
- * turns tracing off).  Every later step writes, per CU and instruction i, s_memrealtime
- * ticks (100 MHz): [0] leader starts i, [1] its inputs are all present, [2] activation
- * staged, [3] leader finished i (incl. attention merge / argmax), [4..7] compute wave
- * 0..3 finished i.  Errors: MK_ESTATE before a schedule exists, MK_EINVAL if too small. */
+ * borrowed device buffer of uint64 [n_cus][L][10] with L the longest per-CU instruction
+ * list; *required_words receives n_cus * L * 10 (pass dev_buf NULL to query, which also
+ * turns tracing off).  The buffer must start zeroed; every later step writes, per CU and
+ * instruction i, s_memrealtime ticks (100 MHz): [0] leader starts i, [1] it starts
+ * polling i's inputs, [2] the inputs are all present, [3] i's activation slot is free,
+ * [4] activation staged, [5] compute wave 0 starts i, [6] the last compute wave finished
+ * i (a running maximum), [7] leader finished i (incl. attention merge / argmax), [8]
+ * leader saw every compute wave finish i (attention and LM head only), [9] the L2
+ * prefetch wave (when on) finished touching i's pages.
+ * Errors: MK_ESTATE before a schedule exists, MK_EINVAL if too small. */
 int mk_set_trace(mk_ctx* ctx, uint64_t* dev_buf, int64_t capacity_words, int64_t* required_words);
 
 /* Free everything the context allocated (not the borrowed weights or caches). */

@@ -22,6 +22,8 @@ struct mk_ctx {
   bool loaded = false;
   bool needs_reset = false;
   long long watchdog_us = 2000000;
+  int pf_pages = 0;     // L2 prefetch distance beyond the LDS ring, in pages (0: off)
+  int pf_line = 128;    // bytes between prefetch touches
   MkPlan plan;
   const void* kernel = nullptr;   // the step kernel compiled for this shape
   // borrowed weights
@@ -127,6 +129,8 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   p.nslot = c->plan.slots;
   p.s_max = c->plan.s_max;
   p.min_chunk = c->plan.min_chunk;
+  p.pf_pages = c->pf_pages;
+  p.pf_line = c->pf_line;
   p.eps = g.rms_eps;
   p.attn_scale = (float)(1.0 / std::sqrt((double)g.head_dim));
   p.embed = c->embed;
@@ -184,6 +188,10 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
   c->device = hip_device;
   c->n_cus = prop.multiProcessorCount;
   c->kernel = shape_kernel(*cfg)->kernel;
+  // Tuning overrides of the L2 prefetch: distance in pages beyond the ring (0 turns it
+  // off) and bytes between touches.
+  if (const char* e = getenv("MK_PREFETCH_PAGES")) c->pf_pages = std::max(0, std::min(64, atoi(e)));
+  if (const char* e = getenv("MK_PREFETCH_LINE")) c->pf_line = atoi(e) == 64 ? 64 : 128;
   *out = c;
   return MK_OK;
 }

@@ -85,6 +85,7 @@ struct __align__(16) MkShared {
   int done[MK_NC];                          // instructions finished, per compute wave
   int full[MK_MAX_SLOTS];                   // ring slot holds page k once full == k + 1
   int freed[MK_MAX_SLOTS];                  // ring slot's page k consumed once freed == k + 1
+  uint32_t pf_sink[64];                     // landing words of the prefetch wave's loads
   int act_seq;                              // instructions staged by the leader
   int abort_flag;
   uint32_t epoch;                           // tag of this step's words
@@ -273,6 +274,12 @@ __device__ __forceinline__ u64 amax_key(float v, uint32_t idx) {
 __device__ __forceinline__ void trace_mark(const MkParams& p, int i, int slot, int lane) {
   if (p.trace && lane == 0 && i < p.trace_len)
     p.trace[((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + slot] = __builtin_amdgcn_s_memrealtime();
+}
+// Latest of several waves' marks.
+__device__ __forceinline__ void trace_max(const MkParams& p, int i, int slot, int lane) {
+  if (p.trace && lane == 0 && i < p.trace_len)
+    atomicMax(p.trace + ((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + slot,
+              (u64)__builtin_amdgcn_s_memrealtime());
 }
 
 // ------------------------------------------------------------------ step geometry
@@ -532,6 +539,59 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   for (; pend > 0; --pend, oldest += MK_NL)
     if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
+}
+
+// HBM -> L2: one 4-byte load per lane into a scratch LDS word, touching 64 lines.
+__device__ __forceinline__ void touch4(const void* g, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(l) : "memory", "m0");
+}
+
+// Prefetch wave.  It walks the loaders' page sequence and touches every line of page k
+// once page k - NSLOT - pf_pages has been consumed, i.e. it runs pf_pages pages beyond
+// the furthest page the ring could hold, so that weight streaming from HBM continues
+// into L2 while the ring is full and the CU waits for activations; the loaders then
+// find those pages in L2.  Nothing waits for it and no result depends on it.
+template <class S>
+__device__ __forceinline__ void prefetch_wave(const MkParams& p, MkShared<S>& sh, cinstr_t list, int nins,
+                                              const StepGeo& g, int lane) {
+  constexpr int NSLOT = Ring<S>::NSLOT;
+  const int ahead = NSLOT + p.pf_pages, line = p.pf_line;
+  const uint32_t sink = lds_addr(sh.pf_sink);
+  int base = 0;
+  for (int i = 0; i < nins; ++i) {
+    const Dec d = decode<S>(p, list[i], g);
+    lane = opaque(lane);
+    for (int pg = 0; pg < d.np; ++pg) {
+      const int j = base + pg - ahead;   // page j must have been consumed first
+      if (j >= 0 && !wait_flag(p, sh, &sh.freed[j % NSLOT], j + 1, false)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+      }
+      if (d.op == MK_OP_ATTN) {
+        constexpr int ROWB = 2 * S::HD;
+        const int q0 = d.j0 + pg * S::PPP;
+        const int bytes = min(S::PPP, d.ce - q0) * ROWB;
+        for (int o = 0; o < bytes; o += 64 * line) {
+          const int off = min(o + lane * line, bytes - 4);
+          touch4(d.m0 + (size_t)q0 * ROWB + off, sink);
+          touch4(d.m1 + (size_t)q0 * ROWB + off, sink);
+        }
+      } else {
+        const int seg = d.op == MK_OP_O ? 2 * S::NQ : d.op == MK_OP_DOWN ? 2 * S::KC : 2 * S::D;
+        const int rows = min(d.rpp, (d.op == MK_OP_GATEUP ? 2 * d.n : d.n) - pg * d.rpp);
+        for (int r = 0; r < rows; ++r) {
+          const char* rb = row_ptr<S>(d, pg, r);
+          for (int o = 0; o < seg; o += 64 * line) touch4(rb + min(o + lane * line, seg - 4), sink);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // bound the loads in flight
+    }
+    trace_mark(p, i, 9, lane);
+    base += d.np;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Page k for a compute wave, once it has landed (nullptr if the wait was abandoned).
@@ -827,7 +887,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     base += d.np;
     lds_fence();
     if (lane == 0) lds_store(&sh.done[w], i + 1);
-    if (w == 0) trace_mark(p, i, 6, lane);
+    trace_max(p, i, 6, lane);
   }
 }
 
@@ -1214,9 +1274,11 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     trace_mark(p, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
       if (!wait_all_done(p, sh, i + 1, true)) return;
+      trace_mark(p, i, 8, lane);
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
     } else if (in.op == MK_OP_LMHEAD) {
       if (!wait_all_done(p, sh, i + 1, true)) return;
+      trace_mark(p, i, 8, lane);
       lm_finalize<S>(p, sh, epoch, lane);
     }
     trace_mark(p, i, 7, lane);
@@ -1260,5 +1322,6 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   const StepGeo g = step_geo<S>(p, p.pos);
   if (wave < MK_NC) compute_wave<S>(p, sh, ring, list, nins, g, wave, lane, epoch);
   else if (wave < MK_NC + MK_NL) loader_wave<S>(p, sh, ring, list, nins, g, wave - MK_NC, lane);
-  else leader_wave<S>(p, sh, list, nins, g, lane, epoch);
+  else if (wave == MK_NC + MK_NL) leader_wave<S>(p, sh, list, nins, g, lane, epoch);
+  else if (p.pf_pages > 0) prefetch_wave<S>(p, sh, list, nins, g, lane);
 }

@@ -8,11 +8,12 @@
 #include <stdint.h>
 
 // Work-group shape, one work-group per CU: MK_NC compute waves that only read LDS,
-// MK_NL loader waves that only stream pages HBM -> LDS, and one leader wave that
-// waits on dependencies and stages activation vectors.
+// MK_NL loader waves that only stream pages HBM -> LDS, one leader wave that waits on
+// dependencies and stages activation vectors, and one prefetch wave that pulls the
+// pages beyond the ring into L2 while the ring is full.
 #define MK_NC 4
 #define MK_NL 2
-#define MK_NWAVES (MK_NC + MK_NL + 1)
+#define MK_NWAVES (MK_NC + MK_NL + 2)
 #define MK_THREADS (64 * MK_NWAVES)
 #define MK_MAX_SLOTS 16
 #define MK_PAGE_BYTES 16384               // one LDS page: 16 units of 1 KiB
@@ -60,6 +61,8 @@ struct MkCtrl {
 struct MkParams {
   int32_t n_layers, V, max_ctx, n_cus;
   int32_t nslot, s_max, min_chunk;   // nslot: pages in the LDS ring
+  int32_t pf_pages;                  // L2 prefetch distance, in pages beyond the ring (0: off)
+  int32_t pf_line;                   // bytes between the prefetch wave's touches (64 or 128)
   float eps, attn_scale;
   // weights (bf16)
   const uint16_t* embed;
@@ -91,5 +94,7 @@ struct MkParams {
 
 // Trace slots per instruction: [0] leader starts, [1] leader starts polling its
 // inputs, [2] inputs all present, [3] slot free, [4] activation staged, [5] compute
-// wave 0 starts, [6] compute wave 0 done, [7] leader done (attention merge / argmax).
-#define MK_TRACE_SLOTS 8
+// wave 0 starts, [6] last compute wave done, [7] leader done (attention merge /
+// argmax), [8] leader saw every compute wave done (attention / LM head), [9] prefetch
+// wave finished touching the instruction's pages.
+#define MK_TRACE_SLOTS 10
