@@ -78,7 +78,8 @@ struct Shape {
 template <class S>
 struct __align__(16) MkShared {
   float act[MK_NACT][S::ACT];               // staged activation vectors (ring)
-  float part[MK_NC][S::HPG][S::HD + 2];     // attention partials (m, l, o) per compute wave
+  float part[MK_NC / S::HPG][S::HPG][S::HD + 2];   // attention partials (m, l, o) per key subset and head
+  int acnt[MK_MAX_SLOTS];                   // readers done with the attention page in a slot
   float xres[2][MK_MAX_RES_ROWS];           // x rows for the residual of O (0) and DOWN (1)
   float dpart[MK_MAX_NCH][MK_MAX_RES_ROWS]; // down-projection partial sums per chunk
   u64 amax[MK_NC];                          // per-wave argmax keys (LM head)
@@ -718,140 +719,171 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
   return true;
 }
 
-template <int HD, int HPG>
-struct AttnState {
-  float q[HPG][8];
-  float m[HPG], l[HPG];
-  float o[HPG][8];
-};
-
-template <int HD, int HPG>
-__device__ __forceinline__ void attn_init(AttnState<HD, HPG>& st, const float* act, int lane) {
-  constexpr int LPP = HD / 8;
-  const int c = lane % LPP;
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st.q[h][e] = act[h * HD + c * 8 + e];
-      st.o[h][e] = 0.f;
-    }
-    st.m[h] = -INFINITY;
-    st.l[h] = 0.f;
-  }
+template <class S>
+__device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, int h, int s) {
+  return ((((size_t)l * S::HKV + g) * S::HPG + h) * p.s_max + s) * (size_t)(S::HD + 2);
 }
+
+// ------------------------------------------------------------------ attention
+// Compute wave w handles query head h = w % HPG of the item's KV group over the key
+// subset t = w / HPG (pages t, t + NSUB, ... of the split; NSUB = MK_NC / HPG): with four
+// query heads per KV head every wave sees every page and owns its head outright, so no
+// cross-wave merge is needed.  Each page is read by HPG waves and freed by the last.
+template <int HD>
+struct HeadState {
+  float q[8];        // dims 8c.. of the head, c = lane % (HD / 8)
+  float m, l;        // running max and denominator over the lane's positions
+  float o[8];        // running numerator for the lane's dims
+};
 
 // One page of cached keys/values: [npos][HD] keys, then [npos][HD] values.  Lane l holds
 // 8 dims (chunk l % LPP) of position l / LPP of each 1 KiB unit.
-template <int HD, int HPG>
-__device__ __forceinline__ void attn_page(AttnState<HD, HPG>& st, const char* page, int npos, float scale,
-                                          int lane) {
+template <int HD>
+__device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, int npos, float scale, int lane) {
   constexpr int LPP = HD / 8;        // lanes per position
   constexpr int PPU = 64 / LPP;      // positions per 1 KiB unit
   constexpr int MAXU = 8;            // units per key block (16 KiB page)
   const int nu = (npos + PPU - 1) / PPU;
   const int kbytes = npos * HD * 2;
   const int jl = lane / LPP;
-  float s[MAXU][HPG];
+  uint4 kw[MAXU];
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u) kw[u] = *(const uint4*)(page + (u < nu ? u : 0) * 1024 + lane * 16);
+  float s[MAXU];
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
-#pragma unroll
-    for (int h = 0; h < HPG; ++h) s[u][h] = -INFINITY;
-    if (u < nu) {
-      const uint4 kw = *(const uint4*)(page + u * 1024 + lane * 16);
-      const bool valid = u * PPU + jl < npos;
-#pragma unroll
-      for (int h = 0; h < HPG; ++h) {
-        float part = dot8(kw, st.q[h], 0.f);
-        part = LPP == 8 ? sum8(part) : sum16(part);
-        s[u][h] = valid ? part * scale : -INFINITY;
-      }
-    }
+    float part = dot8(kw[u], st.q, 0.f);
+    part = LPP == 8 ? sum8(part) : sum16(part);
+    s[u] = (u < nu && u * PPU + jl < npos) ? part * scale : -INFINITY;
   }
+  float pm = s[0];
 #pragma unroll
-  for (int h = 0; h < HPG; ++h) {
-    float pm = s[0][h];
+  for (int u = 1; u < MAXU; ++u) pm = fmaxf(pm, s[u]);
+  pm = wave_max(pm);
+  const float mn = fmaxf(st.m, pm);
+  const float alpha = st.m == -INFINITY ? 0.f : __expf(st.m - mn);
+  st.m = mn;
+  st.l *= alpha;
 #pragma unroll
-    for (int u = 1; u < MAXU; ++u) pm = fmaxf(pm, s[u][h]);
-    pm = wave_max(pm);
-    const float mn = fmaxf(st.m[h], pm);
-    const float alpha = __expf(st.m[h] - mn);
-    st.m[h] = mn;
-    st.l[h] *= alpha;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.o[h][e] *= alpha;
-  }
+  for (int e = 0; e < 8; ++e) st.o[e] *= alpha;
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
     if (u < nu && u * PPU + jl < npos) {
       const uint4 vw = *(const uint4*)(page + kbytes + u * 1024 + lane * 16);
-      float vf[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
-                     bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
-#pragma unroll
-      for (int h = 0; h < HPG; ++h) {
-        const float pr = __expf(s[u][h] - st.m[h]);
-        st.l[h] += pr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.o[h][e] = fmaf(pr, vf[e], st.o[h][e]);
-      }
+      const float pr = __expf(s[u] - mn);
+      st.l += pr;
+      st.o[0] = fmaf(pr, bf_lo(vw.x), st.o[0]);
+      st.o[1] = fmaf(pr, bf_hi(vw.x), st.o[1]);
+      st.o[2] = fmaf(pr, bf_lo(vw.y), st.o[2]);
+      st.o[3] = fmaf(pr, bf_hi(vw.y), st.o[3]);
+      st.o[4] = fmaf(pr, bf_lo(vw.z), st.o[4]);
+      st.o[5] = fmaf(pr, bf_hi(vw.z), st.o[5]);
+      st.o[6] = fmaf(pr, bf_lo(vw.w), st.o[6]);
+      st.o[7] = fmaf(pr, bf_hi(vw.w), st.o[7]);
     }
   }
 }
 
-// Reduce the wave's state over its position groups and leave (m, l, o) in LDS.  The
-// HPG * 9 sums are independent: each swap step is applied to all of them before the
-// next, so their round trips overlap instead of forming one long chain.
-template <int HD, int HPG>
-__device__ __forceinline__ void attn_publish(AttnState<HD, HPG>& st, float (*part)[HD + 2], int lane) {
-  constexpr int LPP = HD / 8;
-  constexpr int HB = HD == 64 ? HPG : 1;   // heads per batch of independent sums (registers)
-#pragma unroll
-  for (int h0 = 0; h0 < HPG; h0 += HB) {
-#pragma unroll
-    for (int off = LPP; off < 64; off <<= 1) {
-      float t[HB][9];
-#pragma unroll
-      for (int h = 0; h < HB; ++h) {
-        t[h][8] = __shfl_xor(st.l[h0 + h], off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[h][e] = __shfl_xor(st.o[h0 + h][e], off);
-      }
-#pragma unroll
-      for (int h = 0; h < HB; ++h) {
-        st.l[h0 + h] += t[h][8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.o[h0 + h][e] += t[h][e];
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) {
-    if (lane < LPP) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part[h][2 + lane * 8 + e] = st.o[h][e];
-    }
-    if (lane == 0) {
-      part[h][0] = st.m[h];
-      part[h][1] = st.l[h];
-    }
-  }
-}
-
-// Attention over this wave's pages of the split; every wave of an active split
-// publishes a partial (m = -inf, l = 0 when it had no page).
+// The item's cached keys for one head, then (one head per wave) the current position's
+// key and value, and the result: o / l into the attention output (one split) or the
+// split's (m, l, o) words; with several waves per head the partial goes to LDS and the
+// leader combines it.
 template <class S>
 __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
-                                         const float* act, int base, int w, int lane) {
-  AttnState<S::HD, S::HPG> st;
-  attn_init<S::HD, S::HPG>(st, act, lane);
-  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
-    const char* page = page_wait<S>(p, sh, ring_base, base + pg);
+                                         const StepGeo& g, const float* act, int base, int w, int lane,
+                                         uint32_t epoch) {
+  constexpr int HD = S::HD, HPG = S::HPG, LPP = HD / 8, NSUB = MK_NC / HPG, NSLOT = Ring<S>::NSLOT;
+  const int h = w % HPG, t = w / HPG, c = lane % LPP;
+  HeadState<HD> st;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    st.q[e] = act[h * HD + c * 8 + e];
+    st.o[e] = 0.f;
+  }
+  st.m = -INFINITY;
+  st.l = 0.f;
+  for (int pg = t; pg < d.np; pg += NSUB) {
+    const int k = base + pg;
+    const char* page = page_wait<S>(p, sh, ring_base, k);
     if (!page) return false;
     const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
-    attn_page<S::HD, S::HPG>(st, page, npos, p.attn_scale, lane);
-    page_free<S>(sh, base + pg, lane);
+    head_page<HD>(st, page, npos, p.attn_scale, lane);
+    lds_fence();
+    // the page's last reader frees it
+    int old = 0;
+    if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
+    old = __shfl(old, 0);
+    if (old == HPG - 1 && lane == 0) {
+      sh.acnt[k % NSLOT] = 0;
+      lds_store(&sh.freed[k % NSLOT], k + 1);
+    }
   }
-  attn_publish<S::HD, S::HPG>(st, sh.part[w], lane);
+  // Sum over the lanes holding other positions (same dims): xor LPP .. 32.
+#pragma unroll
+  for (int off = LPP; off < 64; off <<= 1) {
+    float tt[9];
+    tt[8] = __shfl_xor(st.l, off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tt[e] = __shfl_xor(st.o[e], off);
+    st.l += tt[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] += tt[e];
+  }
+  if constexpr (NSUB > 1) {
+    float* part = sh.part[t][h];
+    if (lane < LPP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[2 + lane * 8 + e] = st.o[e];
+    }
+    if (lane == 0) {
+      part[0] = st.m;
+      part[1] = st.l;
+    }
+    return true;
+  }
+  // One head per wave: fold in the current position (its key is not in the cache yet).
+  const int s = d.b;
+  const bool has_pos = s == g.s_eff - 1;
+  float M = st.m, L = st.l, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = st.o[e];
+  if (has_pos) {
+    float kc[8], vc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kc[e] = act[HPG * HD + c * 8 + e];
+      vc[e] = act[(HPG + 1) * HD + c * 8 + e];
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc = fmaf(st.q[e], kc[e], sc);
+    sc = (LPP == 8 ? sum8(sc) : sum16(sc)) * p.attn_scale;
+    const float Mn = fmaxf(M, sc);
+    const float a = M == -INFINITY ? 0.f : __expf(M - Mn);
+    const float b = __expf(sc - Mn);
+    L = L * a + b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = fmaf(o[e], a, b * vc[e]);
+    M = Mn;
+  }
+  const int l = d.layer, gi = d.a;
+  if (g.s_eff == 1) {
+    u64* dst = p.ll_o + (size_t)l * S::NQ + (gi * HPG + h) * HD + lane * 8;
+    if (lane < LPP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ll_store(dst + e, o[e] / L, epoch);
+    }
+  } else {
+    u64* dst = p.ll_part + part_index<S>(p, l, gi, h, s);
+    if (lane < LPP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ll_store(dst + 2 + lane * 8 + e, o[e], epoch);
+    }
+    if (lane == 0) {
+      ll_store(dst, M, epoch);
+      ll_store(dst + 1, L, epoch);
+    }
+  }
   return true;
 }
 
@@ -871,7 +903,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     const float* act = sh.act[i % MK_NACT];
     bool ok = true;
     if (d.op == MK_OP_ATTN) {
-      if (d.b < g.s_eff) ok = attn_run<S>(p, sh, ring_base, d, act, base, w, lane);   // inactive splits: nothing
+      if (d.b < g.s_eff) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch);   // inactive: nothing
     } else if (d.op == MK_OP_O) {
       ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
     } else if (d.op == MK_OP_DOWN) {
@@ -895,9 +927,10 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
 // Poll NW words per lane (word k*64 + lane of src lands in wv[k]) until all carry this
 // step's epoch.  The first pass loads every word; while words are missing, each lane
 // re-polls only its first missing word (one load per lane per round trip) and the wave
-// reloads the whole batch once one has arrived: re-polling whole vectors from every CU
-// would compete with the weight stream.  A later load of a location never returns an
-// older value than an earlier one, and each word is written once per step.
+// reloads the whole batch once one has arrived.  Re-polling every missing word each
+// round from every CU was measured to congest the memory system (a 25 % slower step).
+// A later load of a location never returns an older value than an earlier one, and each
+// word is written once per step.
 template <class S, int NW>
 __device__ __forceinline__ bool poll(const MkParams& p, MkShared<S>& sh, const u64* src, u64 (&wv)[NW],
                                      uint32_t epoch, int lane) {
@@ -1080,26 +1113,23 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
   return true;
 }
 
-template <class S>
-__device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, int h, int s) {
-  return ((((size_t)l * S::HKV + g) * S::HPG + h) * p.s_max + s) * (size_t)(S::HD + 2);
-}
-
-// After the compute waves: combine their partials (and the current position's key)
-// into this split's (m, l, o), then either write o (single split), publish the split,
-// and/or merge all splits of one head (CUs with split index < heads per group).  Lane
-// `lane` handles elements lane + 64c of each head.
+// After the compute waves.  With fewer query heads per KV head than compute waves, the
+// waves of one head covered disjoint key subsets: combine their partials (and the
+// current position's key) into this split's (m, l, o), then write o (single split) or
+// publish the split.  Then, with several splits, CUs whose split index is below the
+// heads per group merge one head each over all splits.  Lane `lane` handles elements
+// lane + 64c of each head.
 template <class S>
 __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh, const MkInstr& in,
                                               const StepGeo& g, int i, uint32_t epoch, int lane) {
-  constexpr int HD = S::HD, HPG = S::HPG, E = HD / 64, STRIDE = HD + 2;
+  constexpr int HD = S::HD, HPG = S::HPG, E = HD / 64, STRIDE = HD + 2, NSUB = MK_NC / HPG;
   const int l = in.layer, gi = in.a, s = in.b;
   const float* act = sh.act[i % MK_NACT];
-  if (s < g.s_eff) {
+  if (NSUB > 1 && s < g.s_eff) {
     const bool has_pos = s == g.s_eff - 1;
-    float mw[MK_NC][HPG], lw[MK_NC][HPG], ow[MK_NC][HPG][E], qv[HPG][E], kn[E], vn[E];
+    float mw[NSUB][HPG], lw[NSUB][HPG], ow[NSUB][HPG][E], qv[HPG][E], kn[E], vn[E];
 #pragma unroll
-    for (int w = 0; w < MK_NC; ++w)
+    for (int w = 0; w < NSUB; ++w)
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
         mw[w][h] = sh.part[w][h][0];
@@ -1128,10 +1158,10 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
     for (int h = 0; h < HPG; ++h) {
       float M = sp[h];
 #pragma unroll
-      for (int w = 0; w < MK_NC; ++w) M = fmaxf(M, mw[w][h]);
-      float L = 0.f, wt[MK_NC];
+      for (int w = 0; w < NSUB; ++w) M = fmaxf(M, mw[w][h]);
+      float L = 0.f, wt[NSUB];
 #pragma unroll
-      for (int w = 0; w < MK_NC; ++w) {
+      for (int w = 0; w < NSUB; ++w) {
         wt[w] = mw[w][h] == -INFINITY ? 0.f : __expf(mw[w][h] - M);
         L = fmaf(lw[w][h], wt[w], L);
       }
@@ -1141,7 +1171,7 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
       for (int c = 0; c < E; ++c) {
         float o = wp * vn[c];
 #pragma unroll
-        for (int w = 0; w < MK_NC; ++w) o = fmaf(ow[w][h][c], wt[w], o);
+        for (int w = 0; w < NSUB; ++w) o = fmaf(ow[w][h][c], wt[w], o);
         const int e = c * 64 + lane;
         if (g.s_eff == 1)
           ll_store(p.ll_o + (size_t)l * S::NQ + (gi * HPG + h) * HD + e, o / L, epoch);
@@ -1273,7 +1303,8 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     if (lane == 0) lds_store(&sh.act_seq, i + 1);
     trace_mark(p, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
-      if (!wait_all_done(p, sh, i + 1, true)) return;
+      // Partials in LDS only when several waves share a head; a merge polls global words.
+      if (MK_NC > S::HPG && !wait_all_done(p, sh, i + 1, true)) return;
       trace_mark(p, i, 8, lane);
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
     } else if (in.op == MK_OP_LMHEAD) {
@@ -1305,6 +1336,7 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
     for (int k = 0; k < MK_MAX_SLOTS; ++k) {
       sh.full[k] = 0;
       sh.freed[k] = 0;
+      sh.acnt[k] = 0;
     }
     sh.epoch = __hip_atomic_load(&p.ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int t = p.token_dev ? p.token_dev[0] : p.token;
