@@ -321,6 +321,7 @@ struct RowGeo {
 // An instruction decoded once: everything its pages need, wave-uniform.
 struct Dec {
   int op, layer, r0, n, k0, a, b;
+  int rs;            // row stride of the instruction's rows
   int np;            // pages of the instruction on this CU
   int rpp;           // rows per page (GATEUP: gate and up rows, two per feature)
   const char* m0;    // row 0 of each source matrix, input column k0 applied (bytes)
@@ -333,6 +334,7 @@ template <class S>
 __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, const StepGeo& g) {
   Dec d;
   d.op = in.op; d.layer = in.layer; d.r0 = in.r0; d.n = in.n; d.k0 = in.k0; d.a = in.a; d.b = in.b;
+  d.rs = in.rs;
   d.m0 = d.m1 = d.m2 = nullptr;
   d.j0 = d.ce = 0;
   d.rpp = 0;
@@ -371,10 +373,10 @@ template <class S>
 __device__ __forceinline__ const char* row_ptr(const Dec& d, int pg, int j) {
   const int pr = pg * d.rpp + j;   // row of the instruction
   if (d.op == MK_OP_GATEUP) {
-    const long long f = d.r0 + (pr >> 1);
+    const long long f = d.r0 + (long long)(pr >> 1) * d.rs;
     return ((pr & 1) ? d.m1 : d.m0) + f * (2LL * S::D);
   }
-  const int gr = d.r0 + pr;
+  const int gr = d.r0 + pr * d.rs;
   if (d.op == MK_OP_QKV) {
     if (gr >= S::NQ + S::NKV) return d.m2 + (long long)(gr - S::NQ - S::NKV) * (2 * S::D);
     if (gr >= S::NQ) return d.m1 + (long long)(gr - S::NQ) * (2 * S::D);
@@ -692,10 +694,10 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
       const float up = __shfl_down(v, UP);
       if (valid && (pr & 1) == 0) {
         const float a = (v / (1.0f + __expf(-v))) * up;
-        ll_store(p.ll_a + (size_t)l * S::F + d.r0 + (pr >> 1), a, epoch);
+        ll_store(p.ll_a + (size_t)l * S::F + d.r0 + (pr >> 1) * d.rs, a, epoch);
       }
     } else if (valid) {
-      const int gr = d.r0 + pr;
+      const int gr = d.r0 + pr * d.rs;
       if (d.op == MK_OP_QKV) {
         ll_store(p.ll_qkv + (size_t)l * S::NQKV + qkv_index<S>(gr), v, epoch);
       } else if (d.op == MK_OP_O) {

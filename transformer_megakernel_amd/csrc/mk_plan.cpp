@@ -30,6 +30,7 @@ MkInstr mk(int op, int layer) {
   MkInstr x{};
   x.op = op;
   x.layer = layer;
+  x.rs = 1;
   return x;
 }
 
@@ -122,8 +123,12 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
         }
       }
     }
+    // LM-head rows are dealt round-robin (row cu, cu + n_cus, ...): every CU's page k then
+    // lies next to the other CUs' page k in memory, so the CUs, which advance in step,
+    // spread their reads over all HBM channels instead of sharing one offset pattern.
     MkInstr lm = mk(MK_OP_LMHEAD, c.n_layers);
-    lm.r0 = v0; lm.n = vn; lm.k0 = 0; lm.kn = d;
+    lm.r0 = cu; lm.n = (c.vocab - cu + n_cus - 1) / n_cus; lm.k0 = 0; lm.kn = d; lm.rs = n_cus;
+    (void)v0; (void)vn;
     p.rec.push_back(lm);
     p.off.push_back((int32_t)p.rec.size());
   }
