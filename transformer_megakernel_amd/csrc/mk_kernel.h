@@ -367,50 +367,64 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   return d;
 }
 
-// Address of row j (page-relative) of page `pg`.  GATEUP pages interleave gate(f), up(f),
-// gate(f+1), up(f+1), ...; QKV rows run through Wq, then Wk, then Wv.
-template <class S>
-__device__ __forceinline__ const char* row_ptr(const Dec& d, int pg, int j) {
-  const int pr = pg * d.rpp + j;   // row of the instruction
-  if (d.op == MK_OP_GATEUP) {
+// Address of row pr of the instruction, for one opcode.  GATEUP rows interleave gate(f),
+// up(f), gate(f+1), up(f+1), ...; QKV rows run through Wq, then Wk, then Wv.
+template <class S, int OP>
+__device__ __forceinline__ const char* row_addr(const Dec& d, int pr) {
+  if constexpr (OP == MK_OP_GATEUP) {
     const long long f = d.r0 + (long long)(pr >> 1) * d.rs;
     return ((pr & 1) ? d.m1 : d.m0) + f * (2LL * S::D);
-  }
-  const int gr = d.r0 + pr * d.rs;
-  if (d.op == MK_OP_QKV) {
+  } else if constexpr (OP == MK_OP_QKV) {
+    const int gr = d.r0 + pr * d.rs;
     if (gr >= S::NQ + S::NKV) return d.m2 + (long long)(gr - S::NQ - S::NKV) * (2 * S::D);
     if (gr >= S::NQ) return d.m1 + (long long)(gr - S::NQ) * (2 * S::D);
     return d.m0 + (long long)gr * (2 * S::D);
+  } else {
+    constexpr long long RB = OP == MK_OP_O ? 2 * S::NQ : OP == MK_OP_DOWN ? 2 * S::F : 2 * S::D;
+    return d.m0 + (long long)(d.r0 + pr * d.rs) * RB;
   }
-  if (d.op == MK_OP_O) return d.m0 + (long long)gr * (2 * S::NQ);
-  if (d.op == MK_OP_DOWN) return d.m0 + (long long)gr * (2 * S::F);
-  return d.m0 + (long long)gr * (2 * S::D);
+}
+
+// Row j (page-relative) of page pg, any GEMV opcode.
+template <class S>
+__device__ __forceinline__ const char* row_ptr(const Dec& d, int pg, int j) {
+  const int pr = pg * d.rpp + j;
+  if (d.op == MK_OP_GATEUP) return row_addr<S, MK_OP_GATEUP>(d, pr);
+  if (d.op == MK_OP_QKV) return row_addr<S, MK_OP_QKV>(d, pr);
+  if (d.op == MK_OP_O) return row_addr<S, MK_OP_O>(d, pr);
+  if (d.op == MK_OP_DOWN) return row_addr<S, MK_OP_DOWN>(d, pr);
+  return row_addr<S, MK_OP_LMHEAD>(d, pr);
 }
 
 // Issue the DMA of page pg into the LDS page at `slot`: always 16 loads of 1 KiB so the
-// wave's vmcnt moves in steps of 16; loads past the payload re-read valid bytes.
-template <class S, int SEG>
+// wave's vmcnt moves in steps of 16; loads past the payload re-read valid bytes.  The
+// opcode is a template parameter so that each row's address is formed once per page with
+// no branching between the loads (the vector-memory issue slot is the loader's critical
+// resource).
+template <class S, int OP, int SEG>
 __device__ __forceinline__ void issue_rows(const Dec& d, int pg, uint32_t slot, int lane) {
   using R = RowGeo<SEG>;
-  const int rows = (d.op == MK_OP_GATEUP ? 2 * d.n : d.n) - pg * d.rpp;   // rows from this page on
+  const int rows = (OP == MK_OP_GATEUP ? 2 * d.n : d.n) - pg * d.rpp;   // rows from this page on
   if constexpr (R::WIDE) {
+    const char* rb[R::RPP];
+#pragma unroll
+    for (int j = 0; j < R::RPP; ++j) rb[j] = row_addr<S, OP>(d, pg * R::RPP + (j < rows ? j : 0));
+    const int lo = lane * 16;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int j = u / R::KU, c = u % R::KU;
-      const bool real = u < R::USED && j < rows;
-      const char* rb = row_ptr<S>(d, pg, real ? j : 0);
-      dma16(rb + (real ? c * 1024 : 0) + lane * 16, slot + u * 1024);
+      const bool real = u < R::USED;
+      dma16(real ? rb[j] + c * 1024 + lo : rb[0] + lo, slot + u * 1024);
     }
   } else {
     const int jl = lane / R::LPR, cl = lane % R::LPR;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int j = u * R::RPU + jl;
-      dma16(row_ptr<S>(d, pg, j < rows ? j : 0) + cl * 16, slot + u * 1024);
+      dma16(row_addr<S, OP>(d, pg * R::RPP + (j < rows ? j : 0)) + cl * 16, slot + u * 1024);
     }
   }
 }
-
 template <class S>
 __device__ __forceinline__ void issue_page(const Dec& d, int pg, uint32_t slot, int lane) {
   if (d.op == MK_OP_ATTN) {
@@ -428,9 +442,11 @@ __device__ __forceinline__ void issue_page(const Dec& d, int pg, uint32_t slot, 
     }
     return;
   }
-  if (d.op == MK_OP_O) issue_rows<S, 2 * S::NQ>(d, pg, slot, lane);
-  else if (d.op == MK_OP_DOWN) issue_rows<S, 2 * S::KC>(d, pg, slot, lane);
-  else issue_rows<S, 2 * S::D>(d, pg, slot, lane);
+  if (d.op == MK_OP_GATEUP) issue_rows<S, MK_OP_GATEUP, 2 * S::D>(d, pg, slot, lane);
+  else if (d.op == MK_OP_DOWN) issue_rows<S, MK_OP_DOWN, 2 * S::KC>(d, pg, slot, lane);
+  else if (d.op == MK_OP_QKV) issue_rows<S, MK_OP_QKV, 2 * S::D>(d, pg, slot, lane);
+  else if (d.op == MK_OP_O) issue_rows<S, MK_OP_O, 2 * S::NQ>(d, pg, slot, lane);
+  else issue_rows<S, MK_OP_LMHEAD, 2 * S::D>(d, pg, slot, lane);
 }
 
 // ------------------------------------------------------------------ waits and aborts
