@@ -512,9 +512,17 @@ __device__ __forceinline__ int first_of(int who, int base, int period) {
   return ((who - base) % period + period) % period;
 }
 
-// Loader wave l.  It publishes its pages in order, each once vmcnt shows it complete,
-// keeping at most DEPTH of them unpublished.  While it waits for a slot still in use it
-// keeps publishing what it has in flight: a compute wave may be waiting for one of them.
+// Loader wave l.  It publishes its pages in order, each once vmcnt shows it complete.
+// Two pacing modes, chosen per page:
+//  - demand: the page's instruction is already staged, so compute waves are (or soon will
+//    be) waiting for it; keep up to DEPTH of the wave's pages in flight for bandwidth.
+//  - prefetch: the page is for a later instruction; keep a single page in flight for the
+//    whole CU (the two loaders take turns).  A CU's vector-memory requests are served in
+//    order, so every poll of a dependency and every result store queues behind the bytes
+//    this CU has in flight; while the CU is on the critical path (polling, publishing)
+//    its queue must stay short.
+// While it waits for a slot still in use it keeps publishing what it has in flight: a
+// compute wave may be waiting for one of them.
 template <class S>
 __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, char* ring_base, cinstr_t list,
                                             int nins, const StepGeo& g, int l, int lane) {
@@ -523,6 +531,11 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
   const uint32_t ring = lds_addr(ring_base);
   int oldest = 0, pend = 0;   // own pages issued and not yet published: oldest, then every MK_NL-th
   int base = 0;
+  auto publish_oldest = [&]() {
+    if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
+    oldest += MK_NL;
+    --pend;
+  };
   for (int i = 0; i < nins; ++i) {
     const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
@@ -539,25 +552,29 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
           break;
         }
         wait_vmcnt((pend - 1) * 16);
-        if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
-        oldest += MK_NL;
-        --pend;
+        publish_oldest();
+      }
+      const bool demand = lds_load(&sh.act_seq) >= i + 1;
+      if (!demand && k > 0) {
+        // Prefetch: own pages first (the other loader may be waiting for one), then the
+        // other loader's page k - 1 must have landed.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        while (pend > 0) publish_oldest();
+        if (!wait_flag(p, sh, &sh.full[(k - 1) % NSLOT], k, false)) return;
       }
       issue_page<S>(d, pg, ring + (uint32_t)(slot * MK_PAGE_BYTES), lane);
       if (pend == 0) oldest = k;
       ++pend;
-      if (pend == DEPTH) {   // the oldest is complete once at most (DEPTH - 1) pages are outstanding
-        wait_vmcnt((DEPTH - 1) * 16);
-        if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
-        oldest += MK_NL;
-        --pend;
+      const int depth = demand ? DEPTH : 1;
+      while (pend >= depth) {   // the oldest is complete once at most (pend - 1) pages are outstanding
+        wait_vmcnt((pend - 1) * 16);
+        publish_oldest();
       }
     }
     base += d.np;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  for (; pend > 0; --pend, oldest += MK_NL)
-    if (lane == 0) lds_store(&sh.full[oldest % NSLOT], oldest + 1);
+  while (pend > 0) publish_oldest();
 }
 
 // HBM -> L2: one 4-byte load per lane into a scratch LDS word, touching 64 lines.
