@@ -83,7 +83,7 @@ struct __align__(16) MkShared {
   float xres[2][MK_MAX_RES_ROWS];           // x rows for the residual of O (0) and DOWN (1)
   float dpart[MK_MAX_NCH][MK_MAX_RES_ROWS]; // down-projection partial sums per chunk
   u64 amax[MK_NC];                          // per-wave argmax keys (LM head)
-  int done[MK_NC];                          // instructions finished, per compute wave
+  alignas(16) int done[MK_NC];              // instructions finished, per compute wave
   int full[MK_MAX_SLOTS];                   // ring slot holds page k once full == k + 1
   int freed[MK_MAX_SLOTS];                  // ring slot's page k consumed once freed == k + 1
   uint32_t pf_sink[64];                     // landing words of the prefetch wave's loads
@@ -497,6 +497,15 @@ __device__ __forceinline__ bool wait_flag(const MkParams& p, MkShared<S>& sh, co
 
 template <class S>
 __device__ __forceinline__ bool wait_all_done(const MkParams& p, MkShared<S>& sh, int target, bool leader) {
+  static_assert(MK_NC == 4, "two 8-byte reads of the flags");
+  // Usually all done already: two LDS reads instead of four round trips.
+  const u64 d01 = __hip_atomic_load((const u64*)&sh.done[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const u64 d23 = __hip_atomic_load((const u64*)&sh.done[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const int m = min(min((int)(uint32_t)d01, (int)(uint32_t)(d01 >> 32)), min((int)(uint32_t)d23, (int)(uint32_t)(d23 >> 32)));
+  if (m >= target) {
+    compiler_fence();
+    return true;
+  }
   for (int w = 0; w < MK_NC; ++w)
     if (!wait_flag(p, sh, &sh.done[w], target, leader)) return false;
   return true;
@@ -1016,18 +1025,17 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, c
                                            int res_r0, int res_n, int which, int i, uint32_t epoch, int lane) {
   constexpr int NW = S::D / 64;
   constexpr int BW = NW < 32 ? NW : 32;   // words per lane per batch
-  constexpr int NG = S::D / 128;          // gain pairs per lane: lane holds pairs lane + 64k
-  uint32_t gp[NG];
+  // Gain of element k*64 + lane, loaded into this lane before the poll (one 16-bit load
+  // per element, so no cross-lane exchange afterwards).  Rows wider than one batch load
+  // their gains in the normalising pass instead (registers).
+  constexpr int NGV = NW > BW ? 1 : NW;
+  uint32_t gv[NGV];
+  if constexpr (NW <= BW) {
 #pragma unroll
-  for (int k = 0; k < NG; ++k) gp[k] = ((const uint32_t*)gain)[k * 64 + lane];
+    for (int k = 0; k < NW; ++k) gv[k] = gain[k * 64 + lane];
 #pragma unroll
-  for (int k = 0; k < NG; ++k) pin(gp[k]);
-  // Element k*64 + lane is half (lane & 1) of gain pair 32k + lane/2, which sits in
-  // lane (lane/2 + 32k) % 64 = lane/2 + 32 (k & 1), register gp[k / 2].
-  auto gain_of = [&](int k) {
-    const uint32_t pair = __shfl(gp[k >> 1], (lane >> 1) + 32 * (k & 1));
-    return (lane & 1) ? bf_hi(pair) : bf_lo(pair);
-  };
+    for (int k = 0; k < NW; ++k) pin(gv[k]);
+  }
   trace_mark(p, i, 1, lane);
   float* act = sh.act[i % MK_NACT];
   float ss = 0.f;
@@ -1064,26 +1072,19 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, c
     trace_mark(p, i, 3, lane);
     if (lane < res_n) sh.xres[which][lane] = r;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (act[k * 64 + lane] * rinv) * gain_of(k);
+    for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (act[k * 64 + lane] * rinv) * bf16f(gain[k * 64 + lane]);
   } else {
-    float nv[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) nv[k] = (xv[k] * rinv) * gain_of(k);
-    // Residual rows res_r0 + j (j < res_n <= 64) lie in words k0 and k0 + 1.
-    const int k0 = res_r0 >> 6;
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      a0 = k == k0 ? xv[k] : a0;
-      a1 = k == k0 + 1 ? xv[k] : a1;
-    }
-    const int ridx = res_r0 + lane;
-    const float b0 = __shfl(a0, ridx & 63), b1 = __shfl(a1, ridx & 63);
     if (!slot_free(p, sh, i)) return false;
     trace_mark(p, i, 3, lane);
 #pragma unroll
-    for (int k = 0; k < NW; ++k) act[k * 64 + lane] = nv[k];
-    if (lane < res_n) sh.xres[which][lane] = (ridx >> 6) == k0 ? b0 : b1;
+    for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (xv[k] * rinv) * bf16f((uint16_t)gv[k]);
+    // Residual rows res_r0 + j (j < res_n <= 64): element k*64 + lane is row j of them
+    // when 0 <= j < res_n.
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int j = k * 64 + lane - res_r0;
+      if ((unsigned)j < (unsigned)res_n) sh.xres[which][j] = xv[k];
+    }
   }
   return true;
 }
