@@ -1016,13 +1016,12 @@ __device__ __forceinline__ bool slot_free(const MkParams& p, MkShared<S>& sh, in
 }
 
 // RMSNorm staging: act = x * (1 / sqrt(mean(x^2) + eps)) * g, with x the residual
-// stream (the embedding row for the first layer).  Rows [res_r0, res_r0 + res_n) of the
-// raw x are kept for the residual add of the next O / DOWN instruction (xres[which]).
-// Up to 2048 values stay in registers between the sum of squares and the scaled write;
-// longer vectors are written raw in batches and normalised in place.
+// stream (the embedding row for the first layer).  Up to 2048 values stay in registers
+// between the sum of squares and the scaled write; longer vectors are written raw in
+// batches and normalised in place.
 template <class S>
 __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, const u64* src, const uint16_t* gain,
-                                           int res_r0, int res_n, int which, int i, uint32_t epoch, int lane) {
+                                           int i, uint32_t epoch, int lane) {
   constexpr int NW = S::D / 64;
   constexpr int BW = NW < 32 ? NW : 32;   // words per lane per batch
   // Gain of element k*64 + lane, loaded into this lane before the poll (one 16-bit load
@@ -1068,9 +1067,7 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, c
   const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)S::D + p.eps);
   if constexpr (NW > BW) {
     lds_fence();
-    const float r = lane < res_n ? act[res_r0 + lane] : 0.f;
     trace_mark(p, i, 3, lane);
-    if (lane < res_n) sh.xres[which][lane] = r;
 #pragma unroll
     for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (act[k * 64 + lane] * rinv) * bf16f(gain[k * 64 + lane]);
   } else {
@@ -1078,30 +1075,40 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, c
     trace_mark(p, i, 3, lane);
 #pragma unroll
     for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (xv[k] * rinv) * bf16f((uint16_t)gv[k]);
-    // Residual rows res_r0 + j (j < res_n <= 64): element k*64 + lane is row j of them
-    // when 0 <= j < res_n.
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const int j = k * 64 + lane - res_r0;
-      if ((unsigned)j < (unsigned)res_n) sh.xres[which][j] = xv[k];
-    }
   }
   return true;
 }
 
 template <class S, int N>
 __device__ __forceinline__ bool stage_raw(const MkParams& p, MkShared<S>& sh, const u64* src, int i, uint32_t epoch,
-                                          int lane) {
+                                          int lane, const u64* xrow = nullptr, const uint16_t* erow = nullptr,
+                                          int xn = 0, int which = 0) {
   constexpr int NW = N / 64;
+  // Residual rows of x for the instruction's epilogue (xres[which]), when it has one:
+  // from the link words (produced long before this instruction's inputs) or from the
+  // embedding row; loaded alongside the poll so that they cost no extra round trip.
+  const bool has_x = lane < xn;
+  u64 xr = 0;
+  float ev = 0.f;
+  if (xrow && has_x) xr = ll_load(xrow + lane);
+  if (erow && has_x) ev = bf16f(erow[lane]);
   u64 wv[NW];
   trace_mark(p, i, 1, lane);
   if (!poll<S, NW>(p, sh, src, wv, epoch, lane)) return false;
   trace_mark(p, i, 2, lane);
+  if (xrow) {
+    Waiter<S> wt(true);
+    while (__ballot(has_x && !ll_ok(xr, epoch)) != 0) {
+      if (wt.tick(p, sh)) return false;
+      if (has_x && !ll_ok(xr, epoch)) xr = ll_load(xrow + lane);
+    }
+  }
   if (!slot_free(p, sh, i)) return false;
   trace_mark(p, i, 3, lane);
   float* act = sh.act[i % MK_NACT];
 #pragma unroll
   for (int k = 0; k < NW; ++k) act[k * 64 + lane] = ll_val(wv[k]);
+  if (has_x) sh.xres[which][lane] = xrow ? ll_val(xr) : ev;
   return true;
 }
 
@@ -1319,24 +1326,30 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     switch (in.op) {
       case MK_OP_QKV:
         ok = stage_norm<S>(p, sh, l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D,
-                           ((clayers_t)p.layers)[l].attn_norm, in.res_r0, in.res_n, 0, i, epoch, lane);
+                           ((clayers_t)p.layers)[l].attn_norm, i, epoch, lane);
         break;
       case MK_OP_ATTN:
         if (in.b < g.s_eff) ok = stage_attn<S>(p, sh, in, g, i, epoch, lane);
         break;
       case MK_OP_O:
-        ok = stage_raw<S, S::NQ>(p, sh, p.ll_o + (size_t)l * S::NQ, i, epoch, lane);
+        // residual: x entering the layer (the embedding row for the first layer)
+        ok = stage_raw<S, S::NQ>(p, sh, p.ll_o + (size_t)l * S::NQ, i, epoch, lane,
+                                 l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D + in.r0,
+                                 l == 0 ? p.embed + (size_t)sh.token * S::D + in.r0 : nullptr, in.n, 0);
         break;
       case MK_OP_GATEUP:
-        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l + 1) * S::D, ((clayers_t)p.layers)[l].mlp_norm,
-                           in.res_r0, in.res_n, 1, i, epoch, lane);
+        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l + 1) * S::D, ((clayers_t)p.layers)[l].mlp_norm, i,
+                           epoch, lane);
         break;
       case MK_OP_DOWN:
-        ok = stage_raw<S, S::KC>(p, sh, p.ll_a + (size_t)l * S::F + in.k0, i, epoch, lane);
+        // the last chunk adds the residual: x after attention
+        ok = stage_raw<S, S::KC>(p, sh, p.ll_a + (size_t)l * S::F + in.k0, i, epoch, lane,
+                                 in.a + 1 == S::NCH ? p.ll_x + (size_t)(2 * l + 1) * S::D + in.r0 : nullptr, nullptr,
+                                 in.a + 1 == S::NCH ? in.n : 0, 1);
         break;
       default:  // MK_OP_LMHEAD (its record carries layer = n_layers: the last residual version)
-        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l) * S::D, ((clayers_t)p.layers)[l].attn_norm, 0, 0, 0,
-                           i, epoch, lane);
+        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l) * S::D, ((clayers_t)p.layers)[l].attn_norm, i, epoch,
+                           lane);
         break;
     }
     if (!ok) return;

@@ -99,7 +99,7 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
     split(c.vocab, n_cus, cu, &v0, &vn);
     for (int l = 0; l < c.n_layers; ++l) {
       MkInstr q = mk(MK_OP_QKV, l);
-      q.r0 = q0; q.n = qn; q.k0 = 0; q.kn = d; q.res_r0 = o0; q.res_n = on;
+      q.r0 = q0; q.n = qn; q.k0 = 0; q.kn = d;
       p.rec.push_back(q);
       if (cu < c.n_kv_heads * p.s_max) {
         MkInstr a = mk(MK_OP_ATTN, l);
@@ -113,7 +113,7 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
         p.rec.push_back(o);
       }
       MkInstr gu = mk(MK_OP_GATEUP, l);
-      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d; gu.res_r0 = o0; gu.res_n = on;
+      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d;
       p.rec.push_back(gu);
       if (on > 0) {
         for (int k = 0; k < nch; ++k) {

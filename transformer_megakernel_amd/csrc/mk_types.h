@@ -38,9 +38,9 @@ struct MkInstr {
                           // intermediate features, LM-head vocabulary rows
   int32_t k0, kn;         // input columns [k0, k0 + kn) of every row (a DOWN chunk); else 0, K
   int32_t a, b;           // ATTN: kv head, split index; DOWN: chunk index, chunk count
-  int32_t res_r0, res_n;  // QKV / GATEUP: rows of x kept for the residual of the next O / DOWN
+  int32_t pad0, pad1;     // reserved (zero)
   int32_t rs;             // row stride: the instruction's rows are r0, r0 + rs, ... (GATEUP: features)
-  int32_t pad1;
+  int32_t pad2;
 };
 #define MK_INSTR_WORDS 12
 
