@@ -70,15 +70,14 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
         assert phase == sorted(phase), "list not in phase order"
         o_rows = None
         for r in lst:
-            op, layer, r0, n, k0, kn, a, b, rr0, rn = r[:10]
+            op, layer, r0, n, k0, kn, a, b = r[:8]
             cover.setdefault((op, layer, a if op == OPS["DOWN"] else 0), []).append((r0, n, k0, kn, a, b))
             if op == OPS["QKV"]:
-                o_rows = (rr0, rn)
                 assert (k0, kn) == (0, s.hidden)
             if op == OPS["O"]:
-                assert (r0, n) == o_rows and (k0, kn) == (0, nq)
-            if op == OPS["GATEUP"]:
-                assert (rr0, rn) == o_rows
+                # the staging loads one residual row of x per lane
+                assert (k0, kn) == (0, nq) and 0 < n <= 64
+                o_rows = (r0, n)
             if op == OPS["DOWN"]:
                 assert (r0, n) == o_rows and kn == s.ffn // b and k0 == a * kn
     for l in range(s.n_layers):
