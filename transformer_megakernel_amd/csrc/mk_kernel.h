@@ -217,6 +217,36 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<0x143, 0xc>(v, -INFINITY));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// gfx950 lane swaps (VALU, no LDS round trip).  For a, b per lane, swap32 returns
+// {a[l] | b[l - 32], a[l + 32] | b[l]} (lanes below | from 32), swap16 the same within
+// each 32-lane half with 16-lane rows.  So for the pair (lo, hi) the sum of the two
+// results is lo(l) + lo(partner) in the lower lanes and hi(l) + hi(partner) in the upper
+// ones: one halving step of a cross-lane reduction.
+__device__ __forceinline__ float swap_sum32(float lo, float hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float lo, float hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v of lane l ^ 32, lane l ^ 16.
+__device__ __forceinline__ float xor32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+__device__ __forceinline__ float xor16(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+// v of lane l ^ OFF for OFF in {8, 16, 32}; other distances through LDS permutes.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  if constexpr (OFF == 32) return xor32(v, lane);
+  else if constexpr (OFF == 16) return xor16(v, lane);
+  else if constexpr (OFF == 8) return dpp_f<0x128>(v, 0.f);   // row_ror:8 within 16-lane rows
+  else return __shfl_xor(v, OFF);
+}
 // Sum within aligned groups of G lanes (G a power of two <= 64), in every lane.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
@@ -226,8 +256,8 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (G >= 2) v += dpp_f<0xB1>(v, 0.f);
     if constexpr (G >= 4) v += dpp_f<0x4E>(v, 0.f);
   }
-  if constexpr (G >= 32) v += __shfl_xor(v, 16);
-  if constexpr (G >= 64) v += __shfl_xor(v, 32);
+  if constexpr (G >= 32) v = swap_sum16(v, v);
+  if constexpr (G >= 64) v = swap_sum32(v, v);
   return v;
 }
 
@@ -242,6 +272,11 @@ __device__ __forceinline__ float reduce_rows(float (&v)[N], int lane) {
   for (int s = 0; s < ilog2(N); ++s) {
     const int dist = G >> (s + 1);
     const int n = N >> s;
+    if (dist == 32 || dist == 16) {   // lane swaps: lo kept in the lower lanes, hi in the upper
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) v[i] = dist == 32 ? swap_sum32(v[i], v[i + n / 2]) : swap_sum16(v[i], v[i + n / 2]);
+      continue;
+    }
     // Selects through a bit mask: a lane-dependent choice between two array elements
     // must not become an indexed (private memory) access.
     const uint32_t m = (lane & dist) ? 0xffffffffu : 0u;
@@ -733,7 +768,10 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
     const bool valid = owner && pr < rows_total;
     if (d.op == MK_OP_GATEUP) {
       constexpr int UP = R::WIDE ? SPAN : R::LPR;             // lane distance gate row -> up row
-      const float up = __shfl_down(v, UP);
+      float up;
+      if constexpr (UP == 16) up = xor16(v, lane);   // gate rows sit in the lanes below their up row
+      else if constexpr (UP == 32) up = xor32(v, lane);
+      else up = __shfl_down(v, UP);
       if (valid && (pr & 1) == 0) {
         const float a = (v / (1.0f + __expf(-v))) * up;
         ll_store(p.ll_a + (size_t)l * S::F + d.r0 + (pr >> 1) * d.rs, a, epoch);
@@ -866,9 +904,10 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
 #pragma unroll
   for (int off = LPP; off < 64; off <<= 1) {
     float tt[9];
-    tt[8] = __shfl_xor(st.l, off);
+    tt[8] = off == 8 ? xor_lane<8>(st.l, lane) : off == 16 ? xor_lane<16>(st.l, lane) : xor_lane<32>(st.l, lane);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tt[e] = __shfl_xor(st.o[e], off);
+    for (int e = 0; e < 8; ++e)
+      tt[e] = off == 8 ? xor_lane<8>(st.o[e], lane) : off == 16 ? xor_lane<16>(st.o[e], lane) : xor_lane<32>(st.o[e], lane);
     st.l += tt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.o[e] += tt[e];
@@ -1135,7 +1174,7 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
   for (int j = 0; j < NW; ++j) v[j] = ll_val(wv[j]);
   float pr[NW];   // rotation partners
 #pragma unroll
-  for (int j = 0; j < NW; ++j) pr[j] = HD == 64 ? __shfl_xor(v[j], 32) : v[j ^ 1];
+  for (int j = 0; j < NW; ++j) pr[j] = HD == 64 ? xor32(v[j], lane) : v[j ^ 1];
   const bool has_pos = in.b == g.s_eff - 1;
   uint16_t* kslot = p.kv + ((((size_t)l * 2) * S::HKV + gi) * p.max_ctx + g.pos) * HD;
   uint16_t* vslot = kslot + (size_t)S::HKV * p.max_ctx * HD;
