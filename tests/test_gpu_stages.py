@@ -84,3 +84,9 @@ def test_stages_small_shape_head_dim_128():
 
 def test_stages_llama1b():
     run_stage_check(ModelShape.named("llama1b"), 256, 128, 128, 1234)
+
+
+def test_stages_small_shape_head_dim_128_split_kv():
+    """head_dim 128 with the cached keys split over four CUs per KV head (256 keys each),
+    a fifth split holding only the current position, and the splits merged."""
+    run_stage_check(SMALL128, 1100, 1024, 1024, 5)
