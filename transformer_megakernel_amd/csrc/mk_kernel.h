@@ -819,24 +819,28 @@ struct HeadState {
 };
 
 // One page of cached keys/values: [npos][HD] keys, then [npos][HD] values.  Lane l holds
-// 8 dims (chunk l % LPP) of position l / LPP of each 1 KiB unit.
+// 8 dims (chunk l % LPP) of position l / LPP of each 1 KiB unit.  Every byte of a page
+// is a copy of an attended cache row (the loader re-reads valid rows past the payload),
+// so all key and value units are read unconditionally and positions past npos only get
+// a zero weight: no branches, and the value reads overlap the score arithmetic.
 template <int HD>
 __device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, int npos, float scale, int lane) {
   constexpr int LPP = HD / 8;        // lanes per position
   constexpr int PPU = 64 / LPP;      // positions per 1 KiB unit
   constexpr int MAXU = 8;            // units per key block (16 KiB page)
-  const int nu = (npos + PPU - 1) / PPU;
   const int kbytes = npos * HD * 2;
   const int jl = lane / LPP;
-  uint4 kw[MAXU];
+  uint4 kw[MAXU], vw[MAXU];
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) kw[u] = *(const uint4*)(page + (u < nu ? u : 0) * 1024 + lane * 16);
+  for (int u = 0; u < MAXU; ++u) kw[u] = *(const uint4*)(page + u * 1024 + lane * 16);
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u) vw[u] = *(const uint4*)(page + kbytes + u * 1024 + lane * 16);
   float s[MAXU];
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
     float part = dot8(kw[u], st.q, 0.f);
     part = LPP == 8 ? sum8(part) : sum16(part);
-    s[u] = (u < nu && u * PPU + jl < npos) ? part * scale : -INFINITY;
+    s[u] = u * PPU + jl < npos ? part * scale : -INFINITY;
   }
   float pm = s[0];
 #pragma unroll
@@ -850,19 +854,16 @@ __device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, i
   for (int e = 0; e < 8; ++e) st.o[e] *= alpha;
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
-    if (u < nu && u * PPU + jl < npos) {
-      const uint4 vw = *(const uint4*)(page + kbytes + u * 1024 + lane * 16);
-      const float pr = __expf(s[u] - mn);
-      st.l += pr;
-      st.o[0] = fmaf(pr, bf_lo(vw.x), st.o[0]);
-      st.o[1] = fmaf(pr, bf_hi(vw.x), st.o[1]);
-      st.o[2] = fmaf(pr, bf_lo(vw.y), st.o[2]);
-      st.o[3] = fmaf(pr, bf_hi(vw.y), st.o[3]);
-      st.o[4] = fmaf(pr, bf_lo(vw.z), st.o[4]);
-      st.o[5] = fmaf(pr, bf_hi(vw.z), st.o[5]);
-      st.o[6] = fmaf(pr, bf_lo(vw.w), st.o[6]);
-      st.o[7] = fmaf(pr, bf_hi(vw.w), st.o[7]);
-    }
+    const float pr = __expf(s[u] - mn);   // exactly 0 for positions past npos
+    st.l += pr;
+    st.o[0] = fmaf(pr, bf_lo(vw[u].x), st.o[0]);
+    st.o[1] = fmaf(pr, bf_hi(vw[u].x), st.o[1]);
+    st.o[2] = fmaf(pr, bf_lo(vw[u].y), st.o[2]);
+    st.o[3] = fmaf(pr, bf_hi(vw[u].y), st.o[3]);
+    st.o[4] = fmaf(pr, bf_lo(vw[u].z), st.o[4]);
+    st.o[5] = fmaf(pr, bf_hi(vw[u].z), st.o[5]);
+    st.o[6] = fmaf(pr, bf_lo(vw[u].w), st.o[6]);
+    st.o[7] = fmaf(pr, bf_hi(vw[u].w), st.o[7]);
   }
 }
 

@@ -102,9 +102,12 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
       q.r0 = q0; q.n = qn; q.k0 = 0; q.kn = d;
       p.rec.push_back(q);
       if (cu < c.n_kv_heads * p.s_max) {
+        // KV head cu % Hkv, split cu / Hkv: work-groups are dealt to the XCDs round-robin,
+        // so at short contexts (split 0 only) the KV heads' items sit on different XCDs
+        // instead of all on one.
         MkInstr a = mk(MK_OP_ATTN, l);
-        a.a = cu / p.s_max;
-        a.b = cu % p.s_max;
+        a.a = cu % c.n_kv_heads;
+        a.b = cu / c.n_kv_heads;
         p.rec.push_back(a);
       }
       if (on > 0) {
