@@ -48,6 +48,7 @@ def simulate(shape, plan, pos):
     merged = set()                     # (cu, instr index) items published
     nch = max([int(r[7]) for r in rec if int(r[0]) == DOWN] or [1])
     csz = F // nch
+    fpp = max(1, plan["page_bytes"] // (4 * d))   # gate/up features per page
 
     def group_of_qkv_row(r):
         if r < nq:
@@ -93,7 +94,9 @@ def simulate(shape, plan, pos):
                 elif op == GATEUP:
                     if x_rows[2 * layer + 1] < d:
                         break
-                    for f in range(r0, r0 + n):
+                    rs = int(rec[ptr[c]][10])
+                    for q in range(n):
+                        f = r0 + (q // fpp) * rs + q % fpp
                         a_rows[(layer, f // csz)] += 1
                 elif op == DOWN:
                     if a_rows[(layer, a)] < kn:

@@ -63,6 +63,7 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
     nq, nkv = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
     nqkv = nq + 2 * nkv
     cover = {}
+    feats = {}
     for cu in range(n_cus):
         lst = rec[off[cu]:off[cu + 1]]
         assert lst[-1, 0] == OPS["LMHEAD"]
@@ -72,6 +73,10 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
         for r in lst:
             op, layer, r0, n, k0, kn, a, b = r[:8]
             cover.setdefault((op, layer, a if op == OPS["DOWN"] else 0), []).append((r0, n, k0, kn, a, b))
+            if op == OPS["GATEUP"]:
+                # features come a page group at a time: q -> r0 + (q // fpp) * rs + q % fpp
+                fpp = max(1, P["page_bytes"] // (4 * s.hidden))
+                feats.setdefault(layer, []).extend(r0 + (q // fpp) * int(r[10]) + q % fpp for q in range(n))
             if op == OPS["QKV"]:
                 assert (k0, kn) == (0, s.hidden)
             if op == OPS["O"]:
@@ -81,7 +86,8 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
             if op == OPS["DOWN"]:
                 assert (r0, n) == o_rows and kn == s.ffn // b and k0 == a * kn
     for l in range(s.n_layers):
-        for op, total in ((OPS["QKV"], nqkv), (OPS["O"], s.hidden), (OPS["GATEUP"], s.ffn)):
+        assert sorted(feats[l]) == list(range(s.ffn)), "gate/up features not an exact partition"
+        for op, total in ((OPS["QKV"], nqkv), (OPS["O"], s.hidden)):
             rows = sorted((r0, n) for r0, n, *_ in cover[(op, l, 0)] if n > 0)
             pos = 0
             for r0, n in rows:

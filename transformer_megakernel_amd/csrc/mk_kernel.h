@@ -402,12 +402,20 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   return d;
 }
 
+// Feature of the GATEUP instruction's q-th feature: the features come a page (FPP
+// features) at a time, one page group per rs features of the intermediate.
+template <class S>
+__device__ __forceinline__ int gu_feature(const Dec& d, int q) {
+  constexpr int FPP = MK_PAGE_BYTES / (4 * S::D);
+  return d.r0 + (q / FPP) * d.rs + q % FPP;
+}
+
 // Address of row pr of the instruction, for one opcode.  GATEUP rows interleave gate(f),
 // up(f), gate(f+1), up(f+1), ...; QKV rows run through Wq, then Wk, then Wv.
 template <class S, int OP>
 __device__ __forceinline__ const char* row_addr(const Dec& d, int pr) {
   if constexpr (OP == MK_OP_GATEUP) {
-    const long long f = d.r0 + (long long)(pr >> 1) * d.rs;
+    const long long f = gu_feature<S>(d, pr >> 1);
     return ((pr & 1) ? d.m1 : d.m0) + f * (2LL * S::D);
   } else if constexpr (OP == MK_OP_QKV) {
     const int gr = d.r0 + pr * d.rs;
@@ -774,7 +782,7 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
       else up = __shfl_down(v, UP);
       if (valid && (pr & 1) == 0) {
         const float a = (v / (1.0f + __expf(-v))) * up;
-        ll_store(p.ll_a + (size_t)l * S::F + d.r0 + (pr >> 1) * d.rs, a, epoch);
+        ll_store(p.ll_a + (size_t)l * S::F + gu_feature<S>(d, pr >> 1), a, epoch);
       }
     } else if (valid) {
       const int gr = d.r0 + pr * d.rs;

@@ -95,8 +95,19 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
     int o0, on, q0, qn, f0, fn, v0, vn;
     split(d, n_cus, cu, &o0, &on);
     split(nqkv, n_cus, cu, &q0, &qn);
-    split(c.ffn, n_cus, cu, &f0, &fn);
     split(c.vocab, n_cus, cu, &v0, &vn);
+    // Gate/up features are dealt one page (fpp features) at a time, round-robin over the
+    // CUs: feature page pg goes to CU pg % n_cus.  A CU's first pages then feed the first
+    // down chunk, its next pages the second, and so on, so chunk k is complete once every
+    // CU has passed its k-th quarter, long before the slowest CU finishes, and the down
+    // chunks' staging overlaps the gate/up streaming.  Feature q of the instruction is
+    // r0 + (q / fpp) * rs + q % fpp.
+    const int fpp = std::max(1, MK_PAGE_BYTES / (4 * d));
+    const int fpages = (c.ffn + fpp - 1) / fpp;
+    f0 = cu * fpp;
+    fn = 0;
+    for (int pg = cu; pg < fpages; pg += n_cus) fn += std::min(fpp, c.ffn - pg * fpp);
+    const int fstride = n_cus * fpp;
     for (int l = 0; l < c.n_layers; ++l) {
       MkInstr q = mk(MK_OP_QKV, l);
       q.r0 = q0; q.n = qn; q.k0 = 0; q.kn = d;
@@ -116,7 +127,7 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
         p.rec.push_back(o);
       }
       MkInstr gu = mk(MK_OP_GATEUP, l);
-      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d;
+      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d; gu.rs = fstride;
       p.rec.push_back(gu);
       if (on > 0) {
         for (int k = 0; k < nch; ++k) {
@@ -126,12 +137,10 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
         }
       }
     }
-    // LM-head rows are dealt round-robin (row cu, cu + n_cus, ...): every CU's page k then
-    // lies next to the other CUs' page k in memory, so the CUs, which advance in step,
-    // spread their reads over all HBM channels instead of sharing one offset pattern.
+    // LM-head rows: a contiguous block per CU (measured ahead of dealing rows round-robin:
+    // the last CU finished 8 us after the median CU instead of 14 us).
     MkInstr lm = mk(MK_OP_LMHEAD, c.n_layers);
-    lm.r0 = cu; lm.n = (c.vocab - cu + n_cus - 1) / n_cus; lm.k0 = 0; lm.kn = d; lm.rs = n_cus;
-    (void)v0; (void)vn;
+    lm.r0 = v0; lm.n = vn; lm.k0 = 0; lm.kn = d; lm.rs = 1;
     p.rec.push_back(lm);
     p.off.push_back((int32_t)p.rec.size());
   }

@@ -39,7 +39,8 @@ struct MkInstr {
   int32_t k0, kn;         // input columns [k0, k0 + kn) of every row (a DOWN chunk); else 0, K
   int32_t a, b;           // ATTN: kv head, split index; DOWN: chunk index, chunk count
   int32_t pad0, pad1;     // reserved (zero)
-  int32_t rs;             // row stride: the instruction's rows are r0, r0 + rs, ... (GATEUP: features)
+  int32_t rs;             // row stride: the instruction's rows are r0, r0 + rs, ...; GATEUP:
+                          // features come in page groups of FPP, feature q = r0 + (q / FPP) * rs + q % FPP
   int32_t pad2;
 };
 #define MK_INSTR_WORDS 12
