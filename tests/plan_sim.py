@@ -5,7 +5,8 @@ when every value it reads has been produced:
 
 * QKV(l) reads all of x after layer l-1 (the embedding row for l = 0);
 * ATTN(l, g, s), if split s is active at this position, reads q/k/v of KV head g and
-  publishes its partial (or, with one active split, the group's attention output);
+  publishes its partial; with one active split, items s < heads per group each publish
+  the attention output of query head g * hpg + s;
   a CU whose split index s is below the heads per group then merges head s of group g
   from all active splits (only when there is more than one split);
 * O(l) reads every head's attention output; GATEUP(l) reads all of x after O(l);
@@ -75,11 +76,13 @@ def simulate(shape, plan, pos):
                 elif op == ATTN:
                     g, s = a, b
                     key = (c, ptr[c])
-                    if s < s_eff and key not in merged:
+                    active = s < hpg if s_eff == 1 else s < s_eff
+                    if active and key not in merged:
                         if qkv_rows[(layer, g)] < (hpg + 2) * hd:
                             break
                         if s_eff == 1:
-                            o_heads[layer].update(range(g * hpg, (g + 1) * hpg))
+                            # one split: item (g, s < hpg) computes query head g * hpg + s
+                            o_heads[layer].add(g * hpg + s)
                         else:
                             partials[(layer, g)].add(s)
                         merged.add(key)

@@ -79,6 +79,7 @@ template <class S>
 struct __align__(16) MkShared {
   float act[MK_NACT][S::ACT];               // staged activation vectors (ring)
   float part[MK_NC / S::HPG][S::HPG][S::HD + 2];   // attention partials (m, l, o) per key subset and head
+  static_assert(MK_NC % S::HPG == 0, "query heads per KV head must divide the compute waves");
   int acnt[MK_MAX_SLOTS];                   // readers done with the attention page in a slot
   float xres[2][MK_MAX_RES_ROWS];           // x rows for the residual of O (0) and DOWN (1)
   float dpart[MK_MAX_NCH][MK_MAX_RES_ROWS]; // down-projection partial sums per chunk
@@ -321,7 +322,16 @@ __device__ __forceinline__ void trace_max(const MkParams& p, int i, int slot, in
 // ------------------------------------------------------------------ step geometry
 struct StepGeo {
   int pos, s_eff, chunk;   // attention split of keys 0..pos
+  int qh;                  // one split: item (g, b < HPG) computes query head g * HPG + b
 };
+
+// Attention items in a step.  With one split (short contexts) the first HPG items of a
+// KV group each take one query head over all keys, its four compute waves splitting the
+// keys, so a head's scores are spread over four waves instead of one; with several
+// splits, item (g, s) takes split s of group g for all of the group's heads.
+__device__ __forceinline__ bool attn_active(const StepGeo& g, int b, int hpg) {
+  return g.qh ? b < hpg : b < g.s_eff;
+}
 
 template <class S>
 __device__ __forceinline__ StepGeo step_geo(const MkParams& p, int pos) {
@@ -333,6 +343,7 @@ __device__ __forceinline__ StepGeo step_geo(const MkParams& p, int pos) {
   chunk = (chunk + S::PPP - 1) / S::PPP * S::PPP;
   g.chunk = chunk;
   g.s_eff = (nk + chunk - 1) / chunk;
+  g.qh = g.s_eff == 1;
   return g;
 }
 
@@ -375,9 +386,10 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   d.rpp = 0;
   if (in.op == MK_OP_ATTN) {
     d.np = 0;
-    if (in.b < g.s_eff) {
-      d.j0 = in.b * g.chunk;
-      d.ce = min(min(g.pos + 1, (in.b + 1) * g.chunk), g.pos);   // the current key is not in the cache yet
+    if (attn_active(g, in.b, S::HPG)) {
+      const int sb = g.qh ? 0 : in.b;
+      d.j0 = sb * g.chunk;
+      d.ce = min(min(g.pos + 1, (sb + 1) * g.chunk), g.pos);   // the current key is not in the cache yet
       const int cached = d.ce - d.j0;
       d.np = cached > 0 ? (cached + S::PPP - 1) / S::PPP : 0;
     }
@@ -831,24 +843,27 @@ struct HeadState {
 // is a copy of an attended cache row (the loader re-reads valid rows past the payload),
 // so all key and value units are read unconditionally and positions past npos only get
 // a zero weight: no branches, and the value reads overlap the score arithmetic.
-template <int HD>
-__device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, int npos, float scale, int lane) {
-  constexpr int LPP = HD / 8;        // lanes per position
-  constexpr int PPU = 64 / LPP;      // positions per 1 KiB unit
-  constexpr int MAXU = 8;            // units per key block (16 KiB page)
+//
+// The wave takes units u0, u0 + USTEP, ... of the page (USTEP = 1: all of them).
+template <int HD, int USTEP>
+__device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, int npos, float scale, int lane,
+                                          int u0) {
+  constexpr int LPP = HD / 8;          // lanes per position
+  constexpr int PPU = 64 / LPP;        // positions per 1 KiB unit
+  constexpr int MAXU = 8 / USTEP;      // units per key block (16 KiB page) for this wave
   const int kbytes = npos * HD * 2;
   const int jl = lane / LPP;
   uint4 kw[MAXU], vw[MAXU];
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) kw[u] = *(const uint4*)(page + u * 1024 + lane * 16);
+  for (int u = 0; u < MAXU; ++u) kw[u] = *(const uint4*)(page + (u0 + u * USTEP) * 1024 + lane * 16);
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) vw[u] = *(const uint4*)(page + kbytes + u * 1024 + lane * 16);
+  for (int u = 0; u < MAXU; ++u) vw[u] = *(const uint4*)(page + kbytes + (u0 + u * USTEP) * 1024 + lane * 16);
   float s[MAXU];
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
     float part = dot8(kw[u], st.q, 0.f);
     part = LPP == 8 ? sum8(part) : sum16(part);
-    s[u] = u * PPU + jl < npos ? part * scale : -INFINITY;
+    s[u] = (u0 + u * USTEP) * PPU + jl < npos ? part * scale : -INFINITY;
   }
   float pm = s[0];
 #pragma unroll
@@ -856,13 +871,15 @@ __device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, i
   pm = wave_max(pm);
   const float mn = fmaxf(st.m, pm);
   const float alpha = st.m == -INFINITY ? 0.f : __expf(st.m - mn);
+  // -inf only while the wave has seen no position at all (a unit subset past npos)
+  const float mref = mn == -INFINITY ? 0.f : mn;
   st.m = mn;
   st.l *= alpha;
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.o[e] *= alpha;
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
-    const float pr = __expf(s[u] - mn);   // exactly 0 for positions past npos
+    const float pr = __expf(s[u] - mref);   // exactly 0 for positions past npos
     st.l += pr;
     st.o[0] = fmaf(pr, bf_lo(vw[u].x), st.o[0]);
     st.o[1] = fmaf(pr, bf_hi(vw[u].x), st.o[1]);
@@ -884,7 +901,11 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
                                          const StepGeo& g, const float* act, int base, int w, int lane,
                                          uint32_t epoch) {
   constexpr int HD = S::HD, HPG = S::HPG, LPP = HD / 8, NSUB = MK_NC / HPG, NSLOT = Ring<S>::NSLOT;
-  const int h = w % HPG, t = w / HPG, c = lane % LPP;
+  // q-head mode: head d.b of the group; every wave reads every page and takes units
+  // w, w + MK_NC of it.  Otherwise one head per wave (w % HPG) over pages t, t + NSUB, ...
+  const bool qh = g.qh;
+  const int h = qh ? d.b : w % HPG, t = w / HPG, c = lane % LPP;
+  const int readers = qh ? MK_NC : HPG;
   HeadState<HD> st;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -893,18 +914,21 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
   }
   st.m = -INFINITY;
   st.l = 0.f;
-  for (int pg = t; pg < d.np; pg += NSUB) {
+  for (int pg = qh ? 0 : t; pg < d.np; pg += qh ? 1 : NSUB) {
     const int k = base + pg;
     const char* page = page_wait<S>(p, sh, ring_base, k);
     if (!page) return false;
     const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
-    head_page<HD>(st, page, npos, p.attn_scale, lane);
+    if (qh)
+      head_page<HD, MK_NC>(st, page, npos, p.attn_scale, lane, w);
+    else
+      head_page<HD, 1>(st, page, npos, p.attn_scale, lane, 0);
     lds_fence();
     // the page's last reader frees it
     int old = 0;
     if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
     old = __shfl(old, 0);
-    if (old == HPG - 1 && lane == 0) {
+    if (old == readers - 1 && lane == 0) {
       sh.acnt[k % NSLOT] = 0;
       lds_store(&sh.freed[k % NSLOT], k + 1);
     }
@@ -921,8 +945,9 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.o[e] += tt[e];
   }
-  if constexpr (NSUB > 1) {
-    float* part = sh.part[t][h];
+  if (qh || NSUB > 1) {
+    // partial (m, l, o) for the leader; q-head mode: one slot per wave
+    float* part = qh ? &sh.part[0][0][0] + w * (HD + 2) : sh.part[t][h];
     if (lane < LPP) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[2 + lane * 8 + e] = st.o[e];
@@ -995,7 +1020,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     const float* act = sh.act[i % MK_NACT];
     bool ok = true;
     if (d.op == MK_OP_ATTN) {
-      if (d.b < g.s_eff) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch);   // inactive: nothing
+      if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch);
     } else if (d.op == MK_OP_O) {
       ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
     } else if (d.op == MK_OP_DOWN) {
@@ -1184,7 +1209,8 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
   float pr[NW];   // rotation partners
 #pragma unroll
   for (int j = 0; j < NW; ++j) pr[j] = HD == 64 ? xor32(v[j], lane) : v[j ^ 1];
-  const bool has_pos = in.b == g.s_eff - 1;
+  // one writer of the new key and value: the split holding pos (q-head mode: head 0's item)
+  const bool has_pos = g.qh ? in.b == 0 : in.b == g.s_eff - 1;
   uint16_t* kslot = p.kv + ((((size_t)l * 2) * S::HKV + gi) * p.max_ctx + g.pos) * HD;
   uint16_t* vslot = kslot + (size_t)S::HKV * p.max_ctx * HD;
 #pragma unroll
@@ -1221,6 +1247,45 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
   constexpr int HD = S::HD, HPG = S::HPG, E = HD / 64, STRIDE = HD + 2, NSUB = MK_NC / HPG;
   const int l = in.layer, gi = in.a, s = in.b;
   const float* act = sh.act[i % MK_NACT];
+  if (g.qh) {
+    // q-head mode: combine the compute waves' partials of head s with the current key.
+    if (s >= HPG) return true;
+    const float* pb = &sh.part[0][0][0];
+    float mw[MK_NC], lw[MK_NC], ow[MK_NC][E], kn[E], vn[E];
+    float sp = 0.f;
+#pragma unroll
+    for (int w = 0; w < MK_NC; ++w) {
+      mw[w] = pb[w * STRIDE];
+      lw[w] = pb[w * STRIDE + 1];
+#pragma unroll
+      for (int c = 0; c < E; ++c) ow[w][c] = pb[w * STRIDE + 2 + c * 64 + lane];
+    }
+#pragma unroll
+    for (int c = 0; c < E; ++c) {
+      kn[c] = act[HPG * HD + c * 64 + lane];
+      vn[c] = act[(HPG + 1) * HD + c * 64 + lane];
+      sp = fmaf(act[s * HD + c * 64 + lane], kn[c], sp);
+    }
+    sp = wave_sum(sp) * p.attn_scale;
+    float M = sp;
+#pragma unroll
+    for (int w = 0; w < MK_NC; ++w) M = fmaxf(M, mw[w]);
+    const float wp = __expf(sp - M);
+    float L = wp, wt[MK_NC];
+#pragma unroll
+    for (int w = 0; w < MK_NC; ++w) {
+      wt[w] = mw[w] == -INFINITY ? 0.f : __expf(mw[w] - M);
+      L = fmaf(lw[w], wt[w], L);
+    }
+#pragma unroll
+    for (int c = 0; c < E; ++c) {
+      float o = wp * vn[c];
+#pragma unroll
+      for (int w = 0; w < MK_NC; ++w) o = fmaf(ow[w][c], wt[w], o);
+      ll_store(p.ll_o + (size_t)l * S::NQ + (gi * HPG + s) * HD + c * 64 + lane, o / L, epoch);
+    }
+    return true;
+  }
   if (NSUB > 1 && s < g.s_eff) {
     const bool has_pos = s == g.s_eff - 1;
     float mw[NSUB][HPG], lw[NSUB][HPG], ow[NSUB][HPG][E], qv[HPG][E], kn[E], vn[E];
@@ -1377,7 +1442,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
                            ((clayers_t)p.layers)[l].attn_norm, i, epoch, lane);
         break;
       case MK_OP_ATTN:
-        if (in.b < g.s_eff) ok = stage_attn<S>(p, sh, in, g, i, epoch, lane);
+        if (attn_active(g, in.b, S::HPG)) ok = stage_attn<S>(p, sh, in, g, i, epoch, lane);
         break;
       case MK_OP_O:
         // residual: x entering the layer (the embedding row for the first layer)
@@ -1406,7 +1471,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     trace_mark(p, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
       // Partials in LDS only when several waves share a head; a merge polls global words.
-      if (MK_NC > S::HPG && !wait_all_done(p, sh, i + 1, true)) return;
+      if ((MK_NC > S::HPG || g.qh) && !wait_all_done(p, sh, i + 1, true)) return;
       trace_mark(p, i, 8, lane);
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
     } else if (in.op == MK_OP_LMHEAD) {
