@@ -374,6 +374,9 @@ struct Dec {
   const char* m1;
   const char* m2;
   int j0, ce;        // ATTN: cached keys [j0, ce); m0 / m1 = K / V of (layer, kv head) at key 0
+  int rp;            // GATEUP: leading pages held in compute-wave registers (pages w, w + MK_NC, ...
+                     // by wave w);
+                     // np counts the ring pages that follow them
 };
 
 template <class S>
@@ -384,6 +387,7 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   d.m0 = d.m1 = d.m2 = nullptr;
   d.j0 = d.ce = 0;
   d.rpp = 0;
+  d.rp = 0;
   if (in.op == MK_OP_ATTN) {
     d.np = 0;
     if (attn_active(g, in.b, S::HPG)) {
@@ -402,6 +406,10 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   d.rpp = MK_PAGE_BYTES / seg;
   const int rows = in.op == MK_OP_GATEUP ? 2 * in.n : in.n;
   d.np = (rows + d.rpp - 1) / d.rpp;
+  if (MK_HOLD_PAGES && in.op == MK_OP_GATEUP) {
+    d.rp = min(MK_NC * MK_HOLD_PAGES, d.np);
+    d.np -= d.rp;
+  }
   // Plain selects, not a switch: a switch over runtime values becomes a table in
   // private memory.
   const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
@@ -626,7 +634,7 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
         while (pend > 0) publish_oldest();
         if (!wait_flag(p, sh, &sh.full[(k - 1) % NSLOT], k, false)) return;
       }
-      issue_page<S>(d, pg, ring + (uint32_t)(slot * MK_PAGE_BYTES), lane);
+      issue_page<S>(d, d.rp + pg, ring + (uint32_t)(slot * MK_PAGE_BYTES), lane);
       if (pend == 0) oldest = k;
       ++pend;
       const int depth = demand ? DEPTH : 1;
@@ -680,9 +688,9 @@ __device__ __forceinline__ void prefetch_wave(const MkParams& p, MkShared<S>& sh
         }
       } else {
         const int seg = d.op == MK_OP_O ? 2 * S::NQ : d.op == MK_OP_DOWN ? 2 * S::KC : 2 * S::D;
-        const int rows = min(d.rpp, (d.op == MK_OP_GATEUP ? 2 * d.n : d.n) - pg * d.rpp);
+        const int rows = min(d.rpp, (d.op == MK_OP_GATEUP ? 2 * d.n : d.n) - (d.rp + pg) * d.rpp);
         for (int r = 0; r < rows; ++r) {
-          const char* rb = row_ptr<S>(d, pg, r);
+          const char* rb = row_ptr<S>(d, d.rp + pg, r);
           for (int o = 0; o < seg; o += 64 * line) touch4(rb + min(o + lane * line, seg - 4), sink);
         }
       }
@@ -731,7 +739,8 @@ __device__ __forceinline__ int qkv_index(int row) {
 // in parallel in the lanes that hold them.
 template <class S, int SEG>
 __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
-                                     const float* act, int base, int w, int lane, uint32_t epoch, u64* best) {
+                                     const float* act, int base, int w, int lane, uint32_t epoch, u64* best,
+                                     const uint4 (&hold)[MK_HOLD_N][16]) {
   using R = RowGeo<SEG>;
   // The activation slice is kept in registers for rows of up to 4 KiB; longer rows read
   // it from LDS per unit (it would otherwise take 64 registers).
@@ -747,12 +756,9 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
   }
   const int rows_total = d.op == MK_OP_GATEUP ? 2 * d.n : d.n;
   const int l = d.layer;
-  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
-    const char* page = page_wait<S>(p, sh, ring_base, base + pg);
-    if (!page) return false;
-    uint4 wv[R::USED];
-#pragma unroll
-    for (int u = 0; u < R::USED; ++u) wv[u] = *(const uint4*)(page + u * 1024 + lane * 16);
+  // One page: wv holds its units; ipg is its page in the instruction; kfree the ring page
+  // to release once read (-1: a page held in registers).
+  auto page_body = [&](const uint4 (&wv)[R::USED], int ipg, int kfree) {
     float acc[R::NV];
     if constexpr (R::WIDE && AREG) {
 #pragma unroll
@@ -777,14 +783,14 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
 #pragma unroll
       for (int u = 0; u < 16; ++u) acc[u] = dot8(wv[u], av[0], 0.f);
     }
-    page_free<S>(sh, base + pg, lane);
+    if (kfree >= 0) page_free<S>(sh, kfree, lane);
     const float v = reduce_rows<R::NV, R::G>(acc, lane);
     // The row this lane holds, relative to the page, and whether the lane stores it.
     constexpr int SPAN = R::G / R::NV;                        // lanes holding one value
     const int vi = (lane % R::G) / SPAN;                      // value index
     const int j = R::WIDE ? vi : vi * R::RPU + lane / R::LPR;  // row in the page
     const bool owner = (lane % SPAN) == 0;
-    const int pr = pg * d.rpp + j;                             // row of the instruction
+    const int pr = ipg * d.rpp + j;                            // row of the instruction
     const bool valid = owner && pr < rows_total;
     if (d.op == MK_OP_GATEUP) {
       constexpr int UP = R::WIDE ? SPAN : R::LPR;             // lane distance gate row -> up row
@@ -817,9 +823,56 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
         if (key > *best) *best = key;
       }
     }
+  };
+  if constexpr (SEG == 2 * S::D && R::USED == 16) {
+#pragma unroll
+    for (int h = 0; h < MK_HOLD_PAGES; ++h)
+      if (w + h * MK_NC < d.rp) page_body(hold[h], w + h * MK_NC, -1);
+  }
+  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
+    const char* page = page_wait<S>(p, sh, ring_base, base + pg);
+    if (!page) return false;
+    uint4 wv[R::USED];
+#pragma unroll
+    for (int u = 0; u < R::USED; ++u) wv[u] = *(const uint4*)(page + u * 1024 + lane * 16);
+    page_body(wv, d.rp + pg, base + pg);
   }
   return true;
 }
+
+// 16 bytes from global memory, marked non-temporal (streamed weights).
+__device__ __forceinline__ uint4 ld_nt16(const char* a) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)a);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Loads gate/up page ipg of the instruction straight into registers, laid out as the
+// loaders lay a page out in LDS (unit u of the page in hold[u]).
+template <class S>
+__device__ __forceinline__ void load_hold(const Dec& d, int ipg, int lane, uint4 (&hold)[16]) {
+  using R = RowGeo<2 * S::D>;
+  static_assert(R::USED == 16, "gate/up pages are whole");
+  const int rows = 2 * d.n - ipg * R::RPP;
+  if constexpr (R::WIDE) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = u / R::KU, c = u % R::KU;
+      const char* a = row_addr<S, MK_OP_GATEUP>(d, ipg * R::RPP + (j < rows ? j : 0)) + c * 1024 + lane * 16;
+      hold[u] = ld_nt16(a);
+    }
+  } else {
+    const int jl = lane / R::LPR, cl = lane % R::LPR;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = u * R::RPU + jl;
+      const char* a = row_addr<S, MK_OP_GATEUP>(d, ipg * R::RPP + (j < rows ? j : 0)) + cl * 16;
+      hold[u] = ld_nt16(a);
+    }
+  }
+}
+
+
 
 template <class S>
 __device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, int h, int s) {
@@ -1009,9 +1062,34 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
                                              int nins, const StepGeo& g, int w, int lane, uint32_t epoch) {
   int base = 0;   // ring number of the instruction's first page
   u64 best = 0;
+  // A gate/up page held in registers: loaded once the layer's QKV is done, i.e. while
+  // the CU waits for attention and the O projection and its LDS ring is full, so that
+  // four more pages per CU stream during that wait.  hold_for: the instruction it is for.
+  uint4 hold[MK_HOLD_N][16];
+  int hold_for = -1;
   for (int i = 0; i < nins; ++i) {
     const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
+    if (MK_HOLD_PAGES && d.op == MK_OP_QKV) {
+      // this layer's GATEUP follows within three records (ATTN, O)
+      for (int j = i + 1; j < i + 4 && j < nins; ++j) {
+        const MkInstr r = list[j];
+        if (r.op == MK_OP_GATEUP) {
+          const Dec dg = decode<S>(p, r, g);
+#pragma unroll
+          for (int h = 0; h < MK_HOLD_PAGES; ++h)
+            if (w + h * MK_NC < dg.rp) load_hold<S>(dg, w + h * MK_NC, lane, hold[h]);
+          hold_for = j;
+          break;
+        }
+      }
+    }
+    if (MK_HOLD_PAGES && d.op == MK_OP_GATEUP && hold_for != i) {
+#pragma unroll
+      for (int h = 0; h < MK_HOLD_PAGES; ++h)   // not loaded ahead (no QKV before it in the list)
+        if (w + h * MK_NC < d.rp) load_hold<S>(d, w + h * MK_NC, lane, hold[h]);
+      hold_for = i;
+    }
     if (!wait_flag(p, sh, &sh.act_seq, i + 1, false)) return;
     // The last down chunk adds the partial sums of the earlier chunks, which any wave
     // may have produced: wait until every wave has finished the previous instruction.
@@ -1022,11 +1100,11 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     if (d.op == MK_OP_ATTN) {
       if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch);
     } else if (d.op == MK_OP_O) {
-      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
+      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold);
     } else if (d.op == MK_OP_DOWN) {
-      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
+      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold);
     } else {
-      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best);
+      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold);
     }
     if (!ok) return;
     if (d.op == MK_OP_LMHEAD) {
