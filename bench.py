@@ -74,6 +74,33 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
+def read_ceiling(mib: int) -> None:
+    """Plain streaming kernels for comparison, timed with events over 20 passes: torch's
+    float32 sum over ``mib`` MiB (a read, a few bytes written) and an elementwise copy
+    (``mib`` MiB read and written).  Prints the median GB/s of each."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    out = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        ev[0].record()
+        for i in range(20):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(20))[10]
+
+    t_sum = timed(lambda: torch.sum(src, dim=0, out=out))
+    t_copy = timed(lambda: dst.copy_(src))
+    print(json.dumps({"bytes": n, "sum_read_gb_per_s": round(n / t_sum / 1e6, 1),
+                      "copy_read_plus_write_gb_per_s": round(2 * n / t_copy / 1e6, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,12 +108,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama1b_ctx128", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-ceiling", type=int, default=0, metavar="MIB",
+                    help="only time plain streaming kernels (torch sum, copy) over MIB MiB and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a plain copy kernel of known "
                          "size, to calibrate the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.read_ceiling:
+        read_ceiling(args.read_ceiling)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "

@@ -183,6 +183,11 @@ def test_llama1b_context_1024_greedy(llama1b):
     greedy_compare(M, 1234, 1024, 4)
 
 
+def test_llama1b_context_700_three_splits(llama1b):
+    """701 keys: three splits of 256 keys per KV head, merged across CUs."""
+    greedy_compare(llama1b, 4321, 700, 2)
+
+
 def test_llama1b_context_8192_split_kv_repeatable(llama1b):
     M = llama1b
     extra = synth.make_kv_cache(M.shape, 8192, 8192, seed=12, device=DEV)
