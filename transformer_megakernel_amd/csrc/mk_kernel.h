@@ -1563,7 +1563,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
 
 }  // namespace mkdev
 
-// One decode step.  Grid: one work-group per CU (all resident: cooperative launch).
+// One decode step.  Grid: one work-group per CU, all resident at once (one fits per CU).
 template <class S>
 __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   using namespace mkdev;
