@@ -374,10 +374,14 @@ struct Dec {
   const char* m1;
   const char* m2;
   int j0, ce;        // ATTN: cached keys [j0, ce); m0 / m1 = K / V of (layer, kv head) at key 0
-  int rp;            // GATEUP: leading pages held in compute-wave registers (pages w, w + MK_NC, ...
-                     // by wave w);
+  int rp, rw;        // leading pages held in compute-wave registers: page j by wave rw + j;
                      // np counts the ring pages that follow them
 };
+
+// Down pages can be held in registers when they are whole 16-unit pages (and there are
+// at least two chunks).
+template <class S>
+__device__ constexpr bool hold_down() { return S::NCH >= 2 && RowGeo<2 * S::KC>::USED == 16; }
 
 template <class S>
 __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, const StepGeo& g) {
@@ -387,7 +391,7 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   d.m0 = d.m1 = d.m2 = nullptr;
   d.j0 = d.ce = 0;
   d.rpp = 0;
-  d.rp = 0;
+  d.rp = d.rw = 0;
   if (in.op == MK_OP_ATTN) {
     d.np = 0;
     if (attn_active(g, in.b, S::HPG)) {
@@ -406,10 +410,15 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   d.rpp = MK_PAGE_BYTES / seg;
   const int rows = in.op == MK_OP_GATEUP ? 2 * in.n : in.n;
   d.np = (rows + d.rpp - 1) / d.rpp;
+  // Held pages (see compute_wave): gate/up page w by wave w, and the pages of the last two
+  // down chunks, chunk NCH-2 by waves 0, 1 and chunk NCH-1 by waves 2, 3.
   if (MK_HOLD_PAGES && in.op == MK_OP_GATEUP) {
-    d.rp = min(MK_NC * MK_HOLD_PAGES, d.np);
-    d.np -= d.rp;
+    d.rp = min(MK_NC, d.np);
+  } else if (MK_HOLD_PAGES && in.op == MK_OP_DOWN && hold_down<S>() && in.a >= S::NCH - 2) {
+    d.rp = min(2, d.np);
+    d.rw = 2 * (in.a - (S::NCH - 2));
   }
+  d.np -= d.rp;
   // Plain selects, not a switch: a switch over runtime values becomes a table in
   // private memory.
   const MkLayerPtrs L = ((clayers_t)p.layers)[in.layer < p.n_layers ? in.layer : 0];
@@ -740,7 +749,7 @@ __device__ __forceinline__ int qkv_index(int row) {
 template <class S, int SEG>
 __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
                                      const float* act, int base, int w, int lane, uint32_t epoch, u64* best,
-                                     const uint4 (&hold)[MK_HOLD_N][16]) {
+                                     const uint4 (&hold)[16], int mode) {
   using R = RowGeo<SEG>;
   // The activation slice is kept in registers for rows of up to 4 KiB; longer rows read
   // it from LDS per unit (it would otherwise take 64 registers).
@@ -824,11 +833,12 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
       }
     }
   };
-  if constexpr (SEG == 2 * S::D && R::USED == 16) {
-#pragma unroll
-    for (int h = 0; h < MK_HOLD_PAGES; ++h)
-      if (w + h * MK_NC < d.rp) page_body(hold[h], w + h * MK_NC, -1);
+  // mode 0: the held page (if this wave holds one) and the ring pages; 1: only the held
+  // page; 2: only the ring pages.
+  if constexpr (R::USED == 16) {
+    if (mode != 2 && w >= d.rw && w < d.rw + d.rp) page_body(hold, w - d.rw, -1);
   }
+  if (mode == 1) return true;
   for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
     const char* page = page_wait<S>(p, sh, ring_base, base + pg);
     if (!page) return false;
@@ -849,16 +859,16 @@ __device__ __forceinline__ uint4 ld_nt16(const char* a) {
 
 // Loads gate/up page ipg of the instruction straight into registers, laid out as the
 // loaders lay a page out in LDS (unit u of the page in hold[u]).
-template <class S>
+template <class S, int OP, int SEG>
 __device__ __forceinline__ void load_hold(const Dec& d, int ipg, int lane, uint4 (&hold)[16]) {
-  using R = RowGeo<2 * S::D>;
-  static_assert(R::USED == 16, "gate/up pages are whole");
-  const int rows = 2 * d.n - ipg * R::RPP;
+  using R = RowGeo<SEG>;
+  static_assert(R::USED == 16, "held pages are whole");
+  const int rows = (OP == MK_OP_GATEUP ? 2 * d.n : d.n) - ipg * R::RPP;
   if constexpr (R::WIDE) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int j = u / R::KU, c = u % R::KU;
-      const char* a = row_addr<S, MK_OP_GATEUP>(d, ipg * R::RPP + (j < rows ? j : 0)) + c * 1024 + lane * 16;
+      const char* a = row_addr<S, OP>(d, ipg * R::RPP + (j < rows ? j : 0)) + c * 1024 + lane * 16;
       hold[u] = ld_nt16(a);
     }
   } else {
@@ -866,7 +876,7 @@ __device__ __forceinline__ void load_hold(const Dec& d, int ipg, int lane, uint4
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int j = u * R::RPU + jl;
-      const char* a = row_addr<S, MK_OP_GATEUP>(d, ipg * R::RPP + (j < rows ? j : 0)) + cl * 16;
+      const char* a = row_addr<S, OP>(d, ipg * R::RPP + (j < rows ? j : 0)) + cl * 16;
       hold[u] = ld_nt16(a);
     }
   }
@@ -1062,11 +1072,24 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
                                              int nins, const StepGeo& g, int w, int lane, uint32_t epoch) {
   int base = 0;   // ring number of the instruction's first page
   u64 best = 0;
-  // A gate/up page held in registers: loaded once the layer's QKV is done, i.e. while
-  // the CU waits for attention and the O projection and its LDS ring is full, so that
-  // four more pages per CU stream during that wait.  hold_for: the instruction it is for.
-  uint4 hold[MK_HOLD_N][16];
+  // Held pages.  Each compute wave keeps one weight page in registers (64 VGPRs), loaded
+  // ahead of its instruction with plain non-temporal loads; the loaders skip those pages,
+  // so the LDS ring reaches that much further ahead.  Per layer a wave holds its gate/up
+  // page, loaded once the layer's QKV is done (the ring is full while the CU then waits
+  // for attention and the O projection, so four more pages per CU stream during that
+  // wait), and then a page of one of the last two down chunks, loaded as soon as its
+  // gate/up page is consumed (those pages would otherwise stream only after gate/up).
+  // hold_for: the instruction whose page `hold` holds.
+  uint4 hold[16];
   int hold_for = -1;
+  auto holds = [&](const Dec& x) { return x.rp > 0 && w >= x.rw && w < x.rw + x.rp; };
+  auto load_held = [&](const Dec& x, int j) {
+    if (x.op == MK_OP_GATEUP)
+      load_hold<S, MK_OP_GATEUP, 2 * S::D>(x, w - x.rw, lane, hold);
+    else if constexpr (hold_down<S>())
+      load_hold<S, MK_OP_DOWN, 2 * S::KC>(x, w - x.rw, lane, hold);
+    hold_for = j;
+  };
   for (int i = 0; i < nins; ++i) {
     const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
@@ -1076,20 +1099,26 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
         const MkInstr r = list[j];
         if (r.op == MK_OP_GATEUP) {
           const Dec dg = decode<S>(p, r, g);
-#pragma unroll
-          for (int h = 0; h < MK_HOLD_PAGES; ++h)
-            if (w + h * MK_NC < dg.rp) load_hold<S>(dg, w + h * MK_NC, lane, hold[h]);
-          hold_for = j;
+          if (holds(dg)) load_held(dg, j);
           break;
         }
       }
     }
-    if (MK_HOLD_PAGES && d.op == MK_OP_GATEUP && hold_for != i) {
-#pragma unroll
-      for (int h = 0; h < MK_HOLD_PAGES; ++h)   // not loaded ahead (no QKV before it in the list)
-        if (w + h * MK_NC < d.rp) load_hold<S>(d, w + h * MK_NC, lane, hold[h]);
-      hold_for = i;
+    if constexpr (MK_HOLD_PAGES && hold_down<S>()) {
+      if (d.op == MK_OP_DOWN && d.a == 0) {
+        // this layer's held down pages: chunks NCH-2 and NCH-1 follow within NCH records
+        for (int j = i + 1; j < i + S::NCH && j < nins; ++j) {
+          const MkInstr r = list[j];
+          if (r.op != MK_OP_DOWN) break;
+          const Dec dd = decode<S>(p, r, g);
+          if (holds(dd)) {
+            load_held(dd, j);
+            break;
+          }
+        }
+      }
     }
+    if (MK_HOLD_PAGES && holds(d) && hold_for != i) load_held(d, i);   // not loaded ahead
     if (!wait_flag(p, sh, &sh.act_seq, i + 1, false)) return;
     // The last down chunk adds the partial sums of the earlier chunks, which any wave
     // may have produced: wait until every wave has finished the previous instruction.
@@ -1100,11 +1129,11 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     if (d.op == MK_OP_ATTN) {
       if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch);
     } else if (d.op == MK_OP_O) {
-      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold);
+      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0);
     } else if (d.op == MK_OP_DOWN) {
-      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold);
+      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0);
     } else {
-      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold);
+      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0);
     }
     if (!ok) return;
     if (d.op == MK_OP_LMHEAD) {

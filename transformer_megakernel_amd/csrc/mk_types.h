@@ -19,9 +19,8 @@
 #define MK_PAGE_BYTES 16384               // one LDS page: 16 units of 1 KiB
 #define MK_NACT 2                         // staged activation vectors (ring)
 #ifndef MK_HOLD_PAGES
-#define MK_HOLD_PAGES 1                   // gate/up pages per compute wave held in registers
+#define MK_HOLD_PAGES 1                   // compute waves hold weight pages in registers (0: off)
 #endif
-#define MK_HOLD_N (MK_HOLD_PAGES > 0 ? MK_HOLD_PAGES : 1)
 #define MK_MAX_RES_ROWS 64                // rows of x one CU owns in a residual op
 #define MK_MAX_NCH 4                      // K-chunks of the down projection
 
