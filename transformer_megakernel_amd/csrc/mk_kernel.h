@@ -1093,9 +1093,10 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
   for (int i = 0; i < nins; ++i) {
     const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
-    if (MK_HOLD_PAGES && d.op == MK_OP_QKV) {
-      // this layer's GATEUP follows within three records (ATTN, O)
-      for (int j = i + 1; j < i + 4 && j < nins; ++j) {
+    if (MK_HOLD_PAGES && i > 0 && list[i - 1].op == MK_OP_QKV) {
+      // the wave has finished the layer's QKV; its GATEUP follows within three records
+      // (ATTN, O).  (Issued earlier, while the CU polls for x, the loads slowed that poll.)
+      for (int j = i; j < i + 3 && j < nins; ++j) {
         const MkInstr r = list[j];
         if (r.op == MK_OP_GATEUP) {
           const Dec dg = decode<S>(p, r, g);
