@@ -101,6 +101,94 @@ def read_ceiling(mib: int) -> None:
                       "copy_read_plus_write_gb_per_s": round(2 * n / t_copy / 1e6, 1)}), flush=True)
 
 
+def per_op_baseline(shape, W, kv, tok, pos, steps, warmup):
+    """A conventional decode step for comparison: one PyTorch kernel (or a few) per
+    operation, bf16 weights and matrix-vector products (fp32 accumulation inside the
+    library), fp32 residual stream, run eagerly and replayed from a HIP graph.  Returns
+    its timings, and its logits and next token for a sanity check against the megakernel.
+    It is a baseline only: nothing in the library uses it."""
+    import torch
+    import torch.nn.functional as F
+    L, d, hd, hq, hkv = shape.n_layers, shape.hidden, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    hpg, eps, dev = hq // hkv, shape.rms_eps, "cuda:0"
+    bf = torch.bfloat16
+    wqkv = [torch.cat([W.wq[l], W.wk[l], W.wv[l]], 0).contiguous() for l in range(L)]   # fused, as usual
+    wgu = [torch.cat([W.w_gate[l], W.w_up[l]], 0).contiguous() for l in range(L)]
+    half = hd // 2
+    inv = torch.tensor([shape.rope_theta ** (-2.0 * i / hd) for i in range(half)], dtype=torch.float64)
+    ang = pos * inv
+    cos = torch.cos(ang).float().to(dev)
+    sin = torch.sin(ang).float().to(dev)
+    tok_t = torch.tensor([tok], dtype=torch.long, device=dev)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device=dev)
+    nxt = torch.zeros((), dtype=torch.long, device=dev)
+
+    def rms(x, g):
+        return x * torch.rsqrt(x.pow(2).mean() + eps) * g.float()
+
+    def rope(t):   # t: (heads, hd), rotate-half
+        a, b = t[:, :half], t[:, half:]
+        return torch.cat([a * cos - b * sin, b * cos + a * sin], dim=1)
+
+    def step():
+        x = W.embed.index_select(0, tok_t)[0].float()
+        for l in range(L):
+            qkv = torch.mv(wqkv[l], rms(x, W.attn_norm[l]).to(bf)).float()
+            q = rope(qkv[: hq * hd].view(hq, hd))
+            k = rope(qkv[hq * hd: (hq + hkv) * hd].view(hkv, hd))
+            v = qkv[(hq + hkv) * hd:].view(hkv, hd)
+            kv[l, 0, :, pos, :] = k.to(bf)
+            kv[l, 1, :, pos, :] = v.to(bf)
+            K = kv[l, 0, :, : pos + 1, :].contiguous()            # (hkv, P+1, hd)
+            V = kv[l, 1, :, : pos + 1, :].contiguous()
+            qg = q.view(hkv, hpg, hd).transpose(1, 2).contiguous().to(bf)   # (hkv, hd, hpg)
+            s_ = torch.bmm(K, qg).float() * (1.0 / hd ** 0.5)     # (hkv, P+1, hpg)
+            pr = torch.softmax(s_, dim=1).transpose(1, 2).contiguous().to(bf)   # (hkv, hpg, P+1)
+            o = torch.bmm(pr, V).float().reshape(hq * hd)
+            x = x + torch.mv(W.wo[l], o.to(bf)).float()
+            gu = torch.mv(wgu[l], rms(x, W.mlp_norm[l]).to(bf)).float()
+            a = F.silu(gu[: shape.ffn]) * gu[shape.ffn:]
+            x = x + torch.mv(W.w_down[l], a.to(bf)).float()
+        logits.copy_(torch.mv(W.lm_head, rms(x, W.final_norm).to(bf)).float())
+        nxt.copy_(torch.argmax(logits))
+
+    def timed(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record()
+        for i in range(n):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+        return per[len(per) // 2]
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    eager_us = timed(step, steps)
+    ref_logits, ref_tok = logits.clone(), int(nxt.item())
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    same = True
+    for _ in range(3):   # replays must reproduce the eager result
+        logits.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = same and bool(torch.equal(logits, ref_logits)) and int(nxt.item()) == ref_tok
+    graph_us = timed(graph.replay, steps)
+    return {"eager_us": round(eager_us, 1), "graph_us": round(graph_us, 1), "graph_replays_match_eager": same,
+            "token": ref_tok}, ref_logits
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +196,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama1b_ctx128", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-op-baseline", action="store_true",
+                    help="also time a conventional per-operation decode step (PyTorch kernels, eager and "
+                         "as a HIP graph) on the same inputs and report it beside the megakernel")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="MIB",
                     help="only time plain streaming kernels (torch sum, copy) over MIB MiB and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -218,6 +309,16 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(shape, W, kv, tok, ctx)
+    if args.per_op_baseline and not greedy:
+        print("[bench] per-operation baseline", file=sys.stderr, flush=True)
+        m.decode_step(tok, ctx, kv, logits, nxt, stream)
+        m.sync(stream)
+        mk_logits, mk_tok = logits.clone(), int(nxt.item())
+        res, po_logits = per_op_baseline(shape, W, kv, tok, ctx, max(args.steps // 4, 10), 3)
+        res["megakernel_us"] = round(float(np.percentile(per, 50)), 1)
+        res["same_token_as_megakernel"] = res["token"] == mk_tok
+        res["max_abs_logit_diff_vs_megakernel"] = round(float((po_logits - mk_logits).abs().max()), 4)
+        out["per_op_baseline"] = res
     m.close()
     print(json.dumps(out), flush=True)
 
