@@ -378,10 +378,14 @@ struct Dec {
                      // np counts the ring pages that follow them
 };
 
-// Down pages can be held in registers when they are whole 16-unit pages (and there are
-// at least two chunks).
+// Held pages (see compute_wave) take 64 VGPRs per compute wave: used where the kernel has
+// that room (hidden <= 2048; the 4096-wide instance spills registers already, and holding
+// pages there measured 1.2 % slower).  Down pages can be held when they are whole 16-unit
+// pages and there are at least two chunks.
 template <class S>
-__device__ constexpr bool hold_down() { return S::NCH >= 2 && RowGeo<2 * S::KC>::USED == 16; }
+__device__ constexpr bool hold_pages() { return MK_HOLD_PAGES && S::D <= 2048; }
+template <class S>
+__device__ constexpr bool hold_down() { return hold_pages<S>() && S::NCH >= 2 && RowGeo<2 * S::KC>::USED == 16; }
 
 template <class S>
 __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, const StepGeo& g) {
@@ -412,9 +416,9 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   d.np = (rows + d.rpp - 1) / d.rpp;
   // Held pages (see compute_wave): gate/up page w by wave w, and the pages of the last two
   // down chunks, chunk NCH-2 by waves 0, 1 and chunk NCH-1 by waves 2, 3.
-  if (MK_HOLD_PAGES && in.op == MK_OP_GATEUP) {
+  if (hold_pages<S>() && in.op == MK_OP_GATEUP) {
     d.rp = min(MK_NC, d.np);
-  } else if (MK_HOLD_PAGES && in.op == MK_OP_DOWN && hold_down<S>() && in.a >= S::NCH - 2) {
+  } else if (in.op == MK_OP_DOWN && hold_down<S>() && in.a >= S::NCH - 2) {
     d.rp = min(2, d.np);
     d.rw = 2 * (in.a - (S::NCH - 2));
   }
@@ -1093,7 +1097,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
   for (int i = 0; i < nins; ++i) {
     const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
-    if (MK_HOLD_PAGES && i > 0 && list[i - 1].op == MK_OP_QKV) {
+    if (hold_pages<S>() && i > 0 && list[i - 1].op == MK_OP_QKV) {
       // the wave has finished the layer's QKV; its GATEUP follows within three records
       // (ATTN, O).  (Issued earlier, while the CU polls for x, the loads slowed that poll.)
       for (int j = i; j < i + 3 && j < nins; ++j) {
@@ -1105,7 +1109,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
         }
       }
     }
-    if constexpr (MK_HOLD_PAGES && hold_down<S>()) {
+    if constexpr (hold_down<S>()) {
       if (d.op == MK_OP_DOWN && d.a == 0) {
         // this layer's held down pages: chunks NCH-2 and NCH-1 follow within NCH records
         for (int j = i + 1; j < i + S::NCH && j < nins; ++j) {
@@ -1119,7 +1123,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
         }
       }
     }
-    if (MK_HOLD_PAGES && holds(d) && hold_for != i) load_held(d, i);   // not loaded ahead
+    if (hold_pages<S>() && holds(d) && hold_for != i) load_held(d, i);   // not loaded ahead
     if (!wait_flag(p, sh, &sh.act_seq, i + 1, false)) return;
     // The last down chunk adds the partial sums of the earlier chunks, which any wave
     // may have produced: wait until every wave has finished the previous instruction.
