@@ -1631,8 +1631,18 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   const int nins = ((cint_t)p.plan_off)[cu + 1] - o0;
   cinstr_t list = (cinstr_t)p.plan + o0;
   const StepGeo g = step_geo<S>(p, p.pos);
-  if (wave < MK_NC) compute_wave<S>(p, sh, ring, list, nins, g, wave, lane, epoch);
-  else if (wave < MK_NC + MK_NL) loader_wave<S>(p, sh, ring, list, nins, g, wave - MK_NC, lane);
-  else if (wave == MK_NC + MK_NL) leader_wave<S>(p, sh, list, nins, g, lane, epoch);
-  else if (p.pf_pages > 0) prefetch_wave<S>(p, sh, list, nins, g, lane);
+  // Issue priority within a SIMD (each SIMD runs a compute wave and one other wave): the
+  // leader, which is on the critical path between instructions, first, then the loaders,
+  // which keep the DMA queue full; measured 2-3 us per step faster than equal priorities.
+  if (wave < MK_NC) {
+    compute_wave<S>(p, sh, ring, list, nins, g, wave, lane, epoch);
+  } else if (wave < MK_NC + MK_NL) {
+    __builtin_amdgcn_s_setprio(2);
+    loader_wave<S>(p, sh, ring, list, nins, g, wave - MK_NC, lane);
+  } else if (wave == MK_NC + MK_NL) {
+    __builtin_amdgcn_s_setprio(3);
+    leader_wave<S>(p, sh, list, nins, g, lane, epoch);
+  } else if (p.pf_pages > 0) {
+    prefetch_wave<S>(p, sh, list, nins, g, lane);
+  }
 }
