@@ -541,8 +541,10 @@ struct Waiter {
   bool global_check;
   __device__ __forceinline__ Waiter(bool leader) : t0(__builtin_amdgcn_s_memrealtime()), n(0), global_check(leader) {}
   // true when the wait must be abandoned
-  __device__ __forceinline__ bool tick(const MkParams& p, MkShared<S>& sh) {
-    __builtin_amdgcn_s_sleep(1);
+  // nosleep: spin without s_sleep (LDS waits of the compute and loader waves, which
+  // measured faster that way; the leader's waits, which poll global memory, keep it).
+  __device__ __forceinline__ bool tick(const MkParams& p, MkShared<S>& sh, bool nosleep = false) {
+    if (!nosleep) __builtin_amdgcn_s_sleep(1);
     if (lds_load(&sh.abort_flag)) return true;
     if ((++n & 63) == 0) {
       if (global_check &&
@@ -566,7 +568,7 @@ __device__ __forceinline__ bool wait_flag(const MkParams& p, MkShared<S>& sh, co
   if (lds_load(flag) >= target) { compiler_fence(); return true; }
   Waiter<S> wt(leader);
   while (lds_load(flag) < target)
-    if (wt.tick(p, sh)) return false;
+    if (wt.tick(p, sh, !leader)) return false;
   compiler_fence();
   return true;
 }
@@ -1079,10 +1081,10 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
   // Held pages.  Each compute wave keeps one weight page in registers (64 VGPRs), loaded
   // ahead of its instruction with plain non-temporal loads; the loaders skip those pages,
   // so the LDS ring reaches that much further ahead.  Per layer a wave holds its gate/up
-  // page, loaded once the layer's QKV is done (the ring is full while the CU then waits
-  // for attention and the O projection, so four more pages per CU stream during that
-  // wait), and then a page of one of the last two down chunks, loaded as soon as its
-  // gate/up page is consumed (those pages would otherwise stream only after gate/up).
+  // page, loaded when it reaches the layer's O projection (the ring is full while the CU
+  // waits for attention and the O inputs, so four more pages per CU stream during that
+  // wait), and then a page of one of the last two down chunks, loaded when it reaches the
+  // first down chunk (those pages would otherwise stream only after the first chunks').
   // hold_for: the instruction whose page `hold` holds.
   uint4 hold[16];
   int hold_for = -1;
@@ -1097,9 +1099,10 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
   for (int i = 0; i < nins; ++i) {
     const Dec d = decode<S>(p, list[i], g);
     lane = opaque(lane);
-    if (hold_pages<S>() && i > 0 && list[i - 1].op == MK_OP_QKV) {
-      // the wave has finished the layer's QKV; its GATEUP follows within three records
-      // (ATTN, O).  (Issued earlier, while the CU polls for x, the loads slowed that poll.)
+    if (hold_pages<S>() && d.op == MK_OP_O) {
+      // the wave has reached the layer's O projection; its GATEUP follows.  (Issued at the
+      // layer's start, while the CU polls for x, the loads slowed that poll; issued after
+      // QKV, they were 4 us per step slower than here.)
       for (int j = i; j < i + 3 && j < nins; ++j) {
         const MkInstr r = list[j];
         if (r.op == MK_OP_GATEUP) {
