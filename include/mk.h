@@ -37,11 +37,11 @@ extern "C" {
 #define MK_ENOMEM -6   /* device allocation failed                                    */
 
 /* Model shape and numerics.  The article's model is Llama-3.2-1B: 16 layers, hidden
- * 2048, 32 query / 8 KV heads of 64, SwiGLU 8192, vocab 128256.  Supported here:
- * head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with at most 8 query
- * heads per KV head; hidden, ffn and n_q_heads*head_dim multiples of 256 and at most
- * 4096*? (see mk_create); ffn/4 a multiple of 64 bf16 (the down projection is
- * consumed in 4 chunks, after the article's 4-chunk MLP intermediate). */
+ * 2048, 32 query / 8 KV heads of 64, SwiGLU 8192, vocab 128256.  The kernel is compiled
+ * for a fixed list of widths (hidden, query heads, KV heads, head_dim, ffn): the
+ * Llama-3.2-1B and Llama-3.1-8B shapes (4096, 32, 8, 128, 14336) and three small test
+ * decoders; n_layers, vocab and max_ctx are free.  mk_create rejects other widths with
+ * MK_EINVAL and lists the compiled ones (mk_strerror). */
 typedef struct mk_config {
   int32_t n_layers;
   int32_t hidden;      /* d                                   */
@@ -83,8 +83,12 @@ typedef struct mk_weights {
 typedef struct mk_ctx mk_ctx;
 
 /* Create a context for `cfg` on HIP device `hip_device`.  Validates the shape,
- * queries the device (compute units, LDS) and allocates nothing yet.
- * Errors: MK_EINVAL (null/unsupported shape), MK_EHIP (no such device). */
+ * queries the device (compute units) and checks that one work-group of the step kernel
+ * fits on a CU; allocates nothing yet.  Each step launches one work-group per CU, and
+ * all of them must be resident at once (they wait on each other's results), so a step
+ * only completes once no other kernel holds CUs.
+ * Errors: MK_EINVAL (null/unsupported shape), MK_EHIP (no such device, or the kernel
+ * does not fit on a CU). */
 int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out);
 
 /* Record the weight pointers and build the static schedule: per-CU instruction lists
