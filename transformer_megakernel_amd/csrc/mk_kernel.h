@@ -1084,7 +1084,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
   // page, loaded when it reaches the layer's O projection (the ring is full while the CU
   // waits for attention and the O inputs, so four more pages per CU stream during that
   // wait), and then a page of one of the last two down chunks, loaded when it reaches the
-  // first down chunk (those pages would otherwise stream only after the first chunks').
+  // chunk before that one (those pages would otherwise stream only after the first chunks').
   // hold_for: the instruction whose page `hold` holds.
   uint4 hold[16];
   int hold_for = -1;
@@ -1113,9 +1113,11 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
       }
     }
     if constexpr (hold_down<S>()) {
-      if (d.op == MK_OP_DOWN && d.a == 0) {
-        // this layer's held down pages: chunks NCH-2 and NCH-1 follow within NCH records
-        for (int j = i + 1; j < i + S::NCH && j < nins; ++j) {
+      if (d.op == MK_OP_DOWN) {
+        // a held page of the next down chunk, loaded one chunk ahead: loaded at the first
+        // chunk, the 64 KiB per CU were in flight while the CU polled the next two chunks'
+        // inputs, and those polls queued behind them (14 us per step slower)
+        for (int j = i + 1; j < i + 2 && j < nins; ++j) {
           const MkInstr r = list[j];
           if (r.op != MK_OP_DOWN) break;
           const Dec dd = decode<S>(p, r, g);
