@@ -41,6 +41,17 @@ def stored_traffic(workload: str, n_launch_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu's "Model name", read from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, W, kv, tok, pos, budget_s=20.0):
     """The CPU oracle (NumPy fp32, untuned) on this host, on a bounded sample of steps."""
     import numpy as np
@@ -57,7 +68,8 @@ def cpu_baseline(shape, W, kv, tok, pos, budget_s=20.0):
         if el > budget_s or n >= 8:
             break
     return dict(value=round(n / el, 4), unit="steps/s", cores=int(threads), kind="oracle",
-                sample=f"{n} decode steps of the same workload (NumPy fp32 oracle, {el:.1f} s)")
+                sample=f"{n} decode steps of the same workload (NumPy fp32 oracle, {el:.1f} s)",
+                cpu_model=cpu_model())
 
 
 def copy_calibration(mib: int) -> None:
@@ -74,15 +86,19 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
-def read_ceiling(mib: int) -> None:
-    """Plain streaming kernels for comparison, timed with events over 20 passes: torch's
-    float32 sum over ``mib`` MiB (a read, a few bytes written) and an elementwise copy
-    (``mib`` MiB read and written).  Prints the median GB/s of each."""
+def read_ceiling(mib: int) -> dict:
+    """Plain streaming kernels for comparison, timed with events over 20 passes: the
+    library's hand-written streaming read (mk_stream_read) over a sweep of launch shapes,
+    torch's float32 sum over ``mib`` MiB (a read, a few bytes written) and an elementwise
+    copy (``mib`` MiB read and written).  Prints and returns the median GB/s of each."""
     import torch
+
+    from transformer_megakernel_amd import mk
     n = mib << 20
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     out = torch.empty((), dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
 
     def timed(fn):
         for _ in range(3):
@@ -95,10 +111,39 @@ def read_ceiling(mib: int) -> None:
         torch.cuda.synchronize()
         return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(20))[10]
 
+    sweep = {}
+    for blocks in (256, 512, 1024, 2048, 4096, 8192):
+        for unroll in (4, 8, 16):
+            t = timed(lambda: mk.stream_read(src, sink, blocks, unroll))
+            sweep[f"{blocks}x256 threads, {unroll} loads in flight"] = round(n / t / 1e6, 1)
+    best = max(sweep, key=sweep.get)
     t_sum = timed(lambda: torch.sum(src, dim=0, out=out))
     t_copy = timed(lambda: dst.copy_(src))
-    print(json.dumps({"bytes": n, "sum_read_gb_per_s": round(n / t_sum / 1e6, 1),
-                      "copy_read_plus_write_gb_per_s": round(2 * n / t_copy / 1e6, 1)}), flush=True)
+    res = {"bytes": n, "stream_read_best_gb_per_s": sweep[best], "stream_read_best_shape": best,
+           "stream_read_sweep_gb_per_s": sweep, "torch_sum_read_gb_per_s": round(n / t_sum / 1e6, 1),
+           "torch_copy_read_plus_write_gb_per_s": round(2 * n / t_copy / 1e6, 1)}
+    print(json.dumps(res), flush=True)
+    return res
+
+
+def traced_breakdown(m, shape, step_fn, n_steps: int, path: str, title: str) -> None:
+    """Run ``n_steps`` steps with the per-instruction trace on and write the time
+    breakdown (transformer_megakernel_amd.trace_breakdown) to ``path``."""
+    from transformer_megakernel_amd import trace_breakdown as tb
+    buf = m.enable_trace()
+    P = m.plan()
+    traces = []
+    for _ in range(n_steps):
+        buf.zero_()
+        step_fn()
+        m.sync()
+        traces.append(tb.reshape(buf.cpu().numpy(), P["n_cus"]))
+    m.disable_trace()
+    nch = max(int(r[7]) for r in P["records"] if r[0] == tb.DOWN)
+    rep = tb.report(traces, P, shape.n_layers, nch, title)
+    with open(path, "w") as f:
+        f.write(rep + "\n")
+    print(rep, file=sys.stderr, flush=True)
 
 
 def per_op_baseline(shape, W, kv, tok, pos, steps, warmup):
@@ -185,6 +230,16 @@ def per_op_baseline(shape, W, kv, tok, pos, steps, warmup):
         torch.cuda.synchronize()
         same = same and bool(torch.equal(logits, ref_logits)) and int(nxt.item()) == ref_tok
     graph_us = timed(graph.replay, steps)
+    # Five replays bracketed by a marker kernel (the library's streaming read over 4 KiB):
+    # in a kernel trace of this run, the kernels between two markers are one step.
+    from transformer_megakernel_amd import mk
+    mbuf = torch.zeros(1024, dtype=torch.float32, device=dev)
+    msink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        mk.stream_read(mbuf, msink, 1, 1)
+        graph.replay()
+    mk.stream_read(mbuf, msink, 1, 1)
+    torch.cuda.synchronize()
     return {"eager_us": round(eager_us, 1), "graph_us": round(graph_us, 1), "graph_replays_match_eager": same,
             "token": ref_tok}, ref_logits
 
@@ -199,8 +254,13 @@ def main():
     ap.add_argument("--per-op-baseline", action="store_true",
                     help="also time a conventional per-operation decode step (PyTorch kernels, eager and "
                          "as a HIP graph) on the same inputs and report it beside the megakernel")
+    ap.add_argument("--per-op-record", default="", metavar="PATH",
+                    help="with --per-op-baseline: also write its results (and the oracle comparison) to PATH")
+    ap.add_argument("--breakdown", default="", metavar="PATH",
+                    help="after the timed steps, run 10 traced steps and write the time breakdown to PATH")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="MIB",
-                    help="only time plain streaming kernels (torch sum, copy) over MIB MiB and exit")
+                    help="only time plain streaming kernels (the library's streaming read over a sweep of "
+                         "launch shapes, torch sum, copy) over MIB MiB and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a plain copy kernel of known "
                          "size, to calibrate the HBM byte counters) and exit")
@@ -306,6 +366,10 @@ def main():
             "traffic": traffic,
         },
     }
+    if args.breakdown:
+        print("[bench] traced steps for the time breakdown", file=sys.stderr, flush=True)
+        traced_breakdown(m, shape, lambda: step(0), 10, args.breakdown,
+                         f"Time breakdown: {out['config']['workload']} (bench.py --breakdown)")
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(shape, W, kv, tok, ctx)
@@ -318,7 +382,23 @@ def main():
         res["megakernel_us"] = round(float(np.percentile(per, 50)), 1)
         res["same_token_as_megakernel"] = res["token"] == mk_tok
         res["max_abs_logit_diff_vs_megakernel"] = round(float((po_logits - mk_logits).abs().max()), 4)
+        # both against the oracle (the per-operation step rounds its activations to bf16
+        # before each product, as such steps usually do; the megakernel keeps them fp32)
+        import oracle
+        kvn = kv.detach().cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        ref, ref_tok = oracle.decode_step(shape, W.as_numpy_bits(), kvn, tok, ctx, return_next=True)
+        for name, lg, t in (("per_op", po_logits, res["token"]), ("megakernel", mk_logits, mk_tok)):
+            g = lg.cpu().numpy().astype(np.float64)
+            res[f"{name}_vs_oracle"] = {
+                "max_abs": round(float(np.max(np.abs(g - ref))), 5),
+                "rel_l2": round(float(np.linalg.norm(g - ref) / np.linalg.norm(ref)), 6),
+                "same_token": t == ref_tok}
+        res["launches_and_gaps"] = ("from a kernel trace of this run: profile_summary per_op "
+                                    "(kernels between the marker launches are one graph replay)")
         out["per_op_baseline"] = res
+        if args.per_op_record:
+            with open(args.per_op_record, "w") as f:
+                json.dump(res, f, indent=1)
     m.close()
     print(json.dumps(out), flush=True)
 

@@ -87,47 +87,71 @@ typedef struct mk_ctx mk_ctx;
  * fits on a CU; allocates nothing yet.  Each step launches one work-group per CU, and
  * all of them must be resident at once (they wait on each other's results), so a step
  * only completes once no other kernel holds CUs.
- * Errors: MK_EINVAL (null/unsupported shape), MK_EHIP (no such device, or the kernel
- * does not fit on a CU). */
+ * Serves the article's interpreter, which gives every streaming multiprocessor its own
+ * execution plan (Megakernel article, section "Megakernel: a fusion design from
+ * scratch", interpreter paragraph); here one work-group per CU takes that role.
+ * Errors: MK_EINVAL (null/unsupported shape, mk_strerror names the compiled shapes),
+ * MK_EHIP (no such device, or the kernel does not fit on a CU). */
 int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out);
 
 /* Record the weight pointers and build the static schedule: per-CU instruction lists
- * (article: plans laid out statically before runtime and reused for every token),
- * the device-side communication buffers, the RoPE cos/sin table [max_ctx][hd/2]
- * (fp32, computed in double on the host) and the control block.  Synchronous;
- * allocates with hipMalloc.  May be called again to switch weights.
- * Errors: MK_EINVAL, MK_ENOMEM, MK_EHIP. */
+ * (article: plans laid out statically before runtime and reused for every token,
+ * section "Megakernel: a fusion design from scratch", static-plan paragraph), the
+ * device-side communication buffers, the RoPE cos/sin table [max_ctx][hd/2] (fp32,
+ * computed in double on the host) and the control block.  Synchronous; allocates with
+ * hipMalloc (about 11 MB for the Llama-3.2-1B shape).  May be called again to switch
+ * weights.  Matrices must be 16-byte aligned, gains 4-byte aligned.
+ * Errors: MK_EINVAL (null or misaligned pointer), MK_ENOMEM, MK_EHIP. */
 int mk_load_weights(mk_ctx* ctx, const mk_weights* w);
 
-/* One decode step (asynchronous on `stream`, a hipStream_t; NULL = default stream).
+/* One decode step (asynchronous on `stream`, a hipStream_t; NULL = default stream):
+ * the article's six fused instructions for one token, RMSNorm+QKV+RoPE through the
+ * final RMSNorm + LM head, in one kernel launch (section "Megakernel: a fusion design
+ * from scratch", instruction list; the greedy choice is the plainest reading of
+ * generating one token).
  *   token      input token id, in [0, vocab)
  *   pos        its position; keys 0..pos are attended; 0 <= pos < max_ctx
- *   kv_cache   device bf16 [n_layers][2 (K,V)][n_kv_heads][max_ctx][head_dim];
- *              slots [0, pos) must hold the keys (already rotated) and values of the
- *              prefix; slot pos of every layer is overwritten with the new K, V
- *              (rounded to bf16, round-to-nearest-even); other slots are not written.
- *   logits_out device fp32 [vocab]: logits of the next token.
+ *   kv_cache   device bf16 [n_layers][2 (K,V)][n_kv_heads][max_ctx][head_dim], 16-byte
+ *              aligned; slots [0, pos) must hold the keys (already rotated) and values of
+ *              the prefix; slot pos of every layer is overwritten with the new K, V
+ *              (rounded to bf16, round-to-nearest-even); slots past pos are neither read nor
+ *              written.
+ *   logits_out device fp32 [vocab], 4-byte aligned: logits of the next token.
  *   next_token device int32 [1] or NULL: receives argmax(logits), lowest index on ties.
- * Errors: MK_ESTATE (no weights), MK_ERANGE, MK_EINVAL (null kv/logits), MK_EHIP.
- * A device-side watchdog failure is reported by the next mk_sync(). */
+ * Differs from a bare (token, pos, kv_cache, logits_out) signature by the optional
+ * next_token output and the stream argument (void*, so the header needs no HIP header).
+ * Errors: MK_ESTATE (no weights), MK_ERANGE, MK_EINVAL (null or misaligned buffer),
+ * MK_EHIP.  A device-side failure (MK_ETIMEOUT) is reported by the next mk_sync(); every
+ * step launched after the failed one and before that mk_sync() does nothing (it writes
+ * no cache slot, logits or token).  After such a failure the cache slot `pos` of the
+ * failed step may hold the new K/V of some layers and not of others: run that step
+ * again after mk_sync(). */
 int mk_decode_step(mk_ctx* ctx, int32_t token, int32_t pos, void* kv_cache,
                    float* logits_out, int32_t* next_token, void* stream);
 
 /* As mk_decode_step, but the token is read on the device from token_dev (device
  * int32 [1]) when the step starts — e.g. the previous step's next_token — so a
- * greedy loop needs no host synchronisation between steps.  token_dev and
- * next_token may be the same buffer.  Out-of-range device tokens are clamped to
- * [0, vocab) by the kernel and flagged as MK_ERANGE at the next mk_sync(). */
+ * greedy loop needs no host synchronisation between steps (the article reuses one
+ * schedule for many tokens: section "Megakernel: a fusion design from scratch",
+ * static-plan paragraph).  token_dev and next_token may be the same buffer.
+ * Out-of-range device tokens are clamped to [0, vocab) by the kernel and flagged as
+ * MK_ERANGE at the next mk_sync().  Errors as mk_decode_step, plus MK_EINVAL for a
+ * null or misaligned token_dev. */
 int mk_decode_step_dev(mk_ctx* ctx, const int32_t* token_dev, int32_t pos, void* kv_cache,
                        float* logits_out, int32_t* next_token, void* stream);
 
 /* Wait for the context's outstanding steps on `stream` and surface device-side
- * errors (MK_ETIMEOUT, MK_ERANGE for a clamped device token).  After an error the
- * context resets its device state on the next step. */
+ * errors: MK_ETIMEOUT (a bounded wait expired; the article's counter waits are
+ * unbounded, section "Megakernel: a fusion design from scratch", counter paragraph —
+ * here every wait has a budget), MK_ERANGE for a clamped device token.  After an error
+ * the context resets its device state (communication words, control block) on the
+ * next step.  Errors: MK_EINVAL (null), MK_ESTATE (no weights), MK_EHIP. */
 int mk_sync(mk_ctx* ctx, void* stream);
 
 /* Device-side wait budget in microseconds (default 2,000,000).  Every bounded wait in
- * the kernel gives up after this long, records MK_ETIMEOUT and exits. */
+ * the kernel gives up after this long, records MK_ETIMEOUT and exits; 0 makes every
+ * wait give up at its first round (a step then fails unless no wave ever waits).
+ * Errors: MK_EINVAL (null context, negative budget). */
 int mk_set_watchdog_us(mk_ctx* ctx, int64_t us);
 
 /* Schedule introspection (host only; valid after mk_load_weights or mk_plan_only).
@@ -150,24 +174,42 @@ int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out);
  * NULL to query the offsets only.  Errors: MK_ESTATE before mk_load_weights. */
 int mk_debug_dump(const mk_ctx* ctx, uint64_t* host, int64_t capacity_words, int64_t offsets[6]);
 
-/* Per-instruction timestamp trace (the time breakdown of one forward).  dev_buf is a
- * borrowed device buffer of uint64 [n_cus][L][10] with L the longest per-CU instruction
- * list; *required_words receives n_cus * L * 10 (pass dev_buf NULL to query, which also
- * turns tracing off).  The buffer must start zeroed; every later step writes, per CU and
- * instruction i, s_memrealtime ticks (100 MHz): [0] leader starts i, [1] it starts
- * polling i's inputs, [2] the inputs are all present, [3] i's activation slot is free,
- * [4] activation staged, [5] compute wave 0 starts i, [6] the last compute wave finished
- * i (a running maximum), [7] leader finished i (incl. attention merge / argmax), [8]
- * leader saw every compute wave finish i (attention and LM head only), [9] the L2
- * prefetch wave (when on) finished touching i's pages.
- * Errors: MK_ESTATE before a schedule exists, MK_EINVAL if too small. */
+/* Per-instruction timestamp trace: the MI355X form of the article's time breakdown of
+ * one forward (section "Megakernel: a fusion design from scratch", results paragraph).
+ * dev_buf is a borrowed device buffer of uint64 [n_cus][L][10] with L the longest per-CU
+ * instruction list; *required_words receives n_cus * L * 10 (pass dev_buf NULL to query,
+ * which also turns tracing off).  The buffer must be zeroed before every traced step;
+ * the step writes, per CU and instruction i, s_memrealtime ticks (100 MHz): [0] leader
+ * starts i, [1] it starts polling i's inputs, [2] the inputs are all present, [3] i's
+ * activation slot is free, [4] activation staged, [5] compute wave 0 starts i, [6] the
+ * last compute wave finished i (a running maximum), [7] leader finished i (incl.
+ * attention merge / argmax), [8] leader saw every compute wave finish i (attention and
+ * LM head only), [9] ticks the compute waves spent waiting for i's weight (or cached
+ * key/value) pages to land, summed over the waves (a duration, not a time stamp).
+ * Tracing changes no result.  Errors: MK_ESTATE before a schedule exists, MK_EINVAL if
+ * the buffer is too small or not 8-byte aligned. */
 int mk_set_trace(mk_ctx* ctx, uint64_t* dev_buf, int64_t capacity_words, int64_t* required_words);
 
-/* Free everything the context allocated (not the borrowed weights or caches). */
+/* Free everything the context allocated (not the borrowed weights or caches).  Waits
+ * for nothing: the caller must have synchronised the context's streams.  NULL is a
+ * no-op.  (Host-side teardown of the plan's owner, no citation needed.) */
 void mk_destroy(mk_ctx* ctx);
 
-/* Static text for an MK_* code (for MK_EHIP, the last HIP error of this thread). */
+/* Static text for an MK_* code.  For MK_EHIP and MK_EINVAL it gives the detail of the
+ * failure of this thread's last ABI call, if that call recorded one. */
 const char* mk_strerror(int code);
+
+/* ---- Measurement (not part of the decode path) ---------------------------------
+ * A plain streaming read of `bytes` bytes at device pointer `buf` (both 16-byte
+ * multiples/aligned): `blocks` work-groups of 256 threads, each thread keeping `unroll`
+ * (1, 4, 8 or 16) 16-byte non-temporal loads in flight, grid-stride over the buffer.  It
+ * is the practical HBM read ceiling the decode step's bandwidth is reported against (the
+ * pages model a forward as its bytes over the part's bandwidth: Megakernel article,
+ * section "Why are traditional inference methods so inefficient?", bandwidth paragraph).
+ * `sink` is device uint32 [blocks], written only for an input no caller produces (it
+ * keeps the loads live).  Asynchronous on `stream`; time it with events on that stream.
+ * Errors: MK_EINVAL (bad size, alignment or launch shape), MK_EHIP (launch failed). */
+int mk_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll, void* stream);
 
 /* Library version string. */
 const char* mk_version(void);

@@ -7,6 +7,7 @@ from .decode import (  # noqa: F401
     float_to_bf16,
     gemv,
     greedy_decode,
+    widen_weights,
     rms_norm,
     rope_cos_sin,
     silu,

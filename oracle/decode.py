@@ -34,7 +34,9 @@ is silent the plainest Llama reading is taken:
 
 Weights arrive as uint16 arrays holding bf16 bit patterns and are widened exactly
 (bits << 16) to fp32.  ``dtype`` selects the working precision: float32 is the
-parity reference, float64 serves the pins.
+parity reference, float64 serves the pins.  ``widen_weights`` performs that exact
+widening once up front, for long greedy runs; every result is bit-identical to
+passing the bit patterns (the widening is exact, the arithmetic is the same).
 
 Parity status: every function here is pinned by the tests (closed forms,
 invariants, library special cases, and a brute-force full-sequence forward).
@@ -106,9 +108,27 @@ def attend_one_head(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return p @ V
 
 
+def _values(w: np.ndarray, dtype) -> np.ndarray:
+    """The values of a weight tensor given as bf16 bit patterns (uint16), or already
+    widened exactly to a float type by ``widen_weights``."""
+    if w.dtype == np.uint16:
+        return bf16_to_float(w, dtype)
+    return w.astype(dtype, copy=False)
+
+
+def widen_weights(W: dict) -> dict:
+    """The same weights with every bf16 bit pattern widened exactly to float32, once."""
+    out = {}
+    for k, v in W.items():
+        out[k] = [bf16_to_float(t) for t in v] if isinstance(v, list) else bf16_to_float(v)
+    if W.get("lm_head") is W.get("embed"):
+        out["lm_head"] = out["embed"]
+    return out
+
+
 def gemv(W_bits: np.ndarray, x: np.ndarray) -> np.ndarray:
     """y = W x with W given as bf16 bits [out][in]; widened exactly, product in x's precision."""
-    return bf16_to_float(W_bits, x.dtype) @ x
+    return _values(W_bits, x.dtype) @ x
 
 
 # ---------------------------------------------------------------- the decode step
@@ -130,10 +150,10 @@ def decode_step(cfg, W: dict, kv: np.ndarray, token: int, pos: int, dtype=np.flo
         raise ValueError("pos outside the cache")
     cos, sin = rope_cos_sin(pos, hd, cfg.rope_theta, dtype)
 
-    x = bf16_to_float(W["embed"][token], dtype)
+    x = _values(W["embed"][token], dtype)
     for layer in range(cfg.n_layers):
         # 1. RMSNorm + QKV projection + RoPE (+ append K, V to the cache)
-        n = rms_norm(x, bf16_to_float(W["attn_norm"][layer], dtype), eps)
+        n = rms_norm(x, _values(W["attn_norm"][layer], dtype), eps)
         q = gemv(W["wq"][layer], n).reshape(Hq, hd)
         k = gemv(W["wk"][layer], n).reshape(Hkv, hd)
         v = gemv(W["wv"][layer], n).reshape(Hkv, hd)
@@ -158,7 +178,7 @@ def decode_step(cfg, W: dict, kv: np.ndarray, token: int, pos: int, dtype=np.flo
             trace.setdefault("o", []).append(o.reshape(-1).copy())
             trace.setdefault("x", []).append(x.copy())
         # 4. MLP RMSNorm + SiLU(gate) * up
-        n2 = rms_norm(x, bf16_to_float(W["mlp_norm"][layer], dtype), eps)
+        n2 = rms_norm(x, _values(W["mlp_norm"][layer], dtype), eps)
         a = silu(gemv(W["w_gate"][layer], n2)) * gemv(W["w_up"][layer], n2)
         # 5. down projection + residual
         x = x + gemv(W["w_down"][layer], a)
@@ -166,7 +186,7 @@ def decode_step(cfg, W: dict, kv: np.ndarray, token: int, pos: int, dtype=np.flo
             trace.setdefault("a", []).append(a.copy())
             trace["x"].append(x.copy())
     # 6. final RMSNorm + LM head
-    nf = rms_norm(x, bf16_to_float(W["final_norm"], dtype), eps)
+    nf = rms_norm(x, _values(W["final_norm"], dtype), eps)
     logits = gemv(W["lm_head"], nf)
     if return_next:
         return logits, int(np.argmax(logits))

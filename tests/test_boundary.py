@@ -116,3 +116,47 @@ def test_plan_has_no_deadlock_at_any_position(name, pos):
     m = mk.Megakernel.plan_only(s, 8193, 256)
     done, steps = simulate(s, m.plan(), pos)
     assert done, f"deadlock after {steps} rounds"
+
+
+def _drop(plan, cu, pred):
+    """A copy of ``plan`` with the first record of CU ``cu`` matching ``pred`` removed."""
+    off, rec = plan["offsets"].copy(), plan["records"]
+    idx = next(i for i in range(off[cu], off[cu + 1]) if pred(rec[i]))
+    out = dict(plan)
+    out["records"] = np.delete(rec, idx, axis=0)
+    out["offsets"] = np.where(np.arange(off.size) > cu, off - 1, off)
+    return out
+
+
+def _move_before(plan, cu, pred_moved, pred_anchor):
+    """A copy of ``plan`` where CU ``cu``'s first record matching ``pred_moved`` is moved
+    in front of its first record matching ``pred_anchor``."""
+    off, rec = plan["offsets"], plan["records"].copy()
+    lst = list(range(off[cu], off[cu + 1]))
+    i = next(j for j in lst if pred_moved(rec[j]))
+    a = next(j for j in lst if pred_anchor(rec[j]))
+    assert a < i
+    block = rec[off[cu]:off[cu + 1]].tolist()
+    r = block.pop(i - off[cu])
+    block.insert(a - off[cu], r)
+    rec[off[cu]:off[cu + 1]] = np.array(block, dtype=rec.dtype)
+    out = dict(plan)
+    out["records"] = rec
+    return out
+
+
+@pytest.mark.parametrize("pos", [128, 1024])
+def test_plan_simulator_reports_planted_deadlocks(pos):
+    """The schedule simulator is only a deadlock check if it can fail: a plan missing one
+    CU's QKV rows of a layer (attention then waits for them forever), and a plan where a
+    CU consumes a down-projection chunk before producing its own gate/up features for it
+    (a wait on work queued behind itself), must both be reported as stuck."""
+    from tests.plan_sim import simulate
+    s = ModelShape.named("llama1b")
+    P = mk.Megakernel.plan_only(s, 8193, 256).plan()
+    assert simulate(s, P, pos)[0]
+    missing = _drop(P, 37, lambda r: r[0] == OPS["QKV"] and r[1] == 5)
+    assert not simulate(s, missing, pos)[0]
+    circular = _move_before(P, 11, lambda r: r[0] == OPS["DOWN"] and r[1] == 3 and r[6] == 0,
+                            lambda r: r[0] == OPS["GATEUP"] and r[1] == 3)
+    assert not simulate(s, circular, pos)[0]

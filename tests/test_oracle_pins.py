@@ -216,6 +216,22 @@ def test_fp32_oracle_close_to_fp64_on_tiny_greedy():
     assert max(np.max(np.abs(a - b)) for a, b in zip(l32, l64)) < 1e-4
 
 
+def test_widened_weights_give_bit_identical_steps():
+    """Widening the bf16 weights once up front (for long greedy runs) is exact, so the
+    logits and the cache writes are bit-identical to passing the bit patterns."""
+    shape, W = _tiny()
+    Wf = od.widen_weights(W)
+    assert Wf["lm_head"] is Wf["embed"]
+    for dt in (np.float32, np.float64):
+        kv_a = make_kv_cache(shape, 32, 16, seed=1).view(torch.int16).numpy().view(np.uint16).copy()
+        kv_b = kv_a.copy()
+        for p, t in enumerate([5, 900, 4095]):
+            la = od.decode_step(shape, W, kv_a, t, 16 + p, dt)
+            lb = od.decode_step(shape, Wf, kv_b, t, 16 + p, dt)
+            assert np.array_equal(la, lb)
+        assert np.array_equal(kv_a, kv_b)
+
+
 # ---------------------------------------------------------------- the pins have teeth
 _MUTATIONS = [
     ("g = (h * Hkv) // Hq", "g = h % Hkv"),                                    # GQA index

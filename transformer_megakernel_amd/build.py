@@ -7,7 +7,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mk_api.hip")
+# the decode kernel + C ABI + scheduler, and the measurement kernels
+SRCS = [os.path.join(PKG, "csrc", "mk_api.hip"), os.path.join(PKG, "csrc", "mk_measure.hip")]
 LIB = os.path.join(PKG, "libmk.so")
 
 HIPCC_FLAGS = [
@@ -26,9 +27,10 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/mk_api.hip (kernel + C ABI + scheduler) into libmk.so; return its path."""
+    """Compile csrc/mk_api.hip (kernel + C ABI + scheduler) and csrc/mk_measure.hip
+    (measurement kernels) into libmk.so; return its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

@@ -71,6 +71,15 @@ const ShapeKernel* shape_kernel(const mk_config& c) {
   return nullptr;
 }
 
+// Every ABI call starts with a clean message, so that mk_strerror never reports a detail
+// left behind by an earlier, unrelated failure.
+void abi_enter() { g_hip_msg[0] = 0; }
+
+int einval(const char* why) {
+  snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", why);
+  return MK_EINVAL;
+}
+
 int hip_fail(hipError_t e, const char* what) {
   snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s", what, hipGetErrorString(e));
   return MK_EHIP;
@@ -110,9 +119,14 @@ int reset_device_state(mk_ctx* c, hipStream_t s) {
 
 int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void* kv, float* logits,
            int32_t* next_token, hipStream_t s) {
+  abi_enter();
   if (!c) return MK_EINVAL;
   if (!c->loaded || c->plan_only) return MK_ESTATE;
-  if (!kv || !logits) return MK_EINVAL;
+  if (!kv || !logits) return einval("kv_cache and logits_out must not be null");
+  // Cache rows are streamed with 16-byte loads; logits, tokens are 4-byte words.
+  if ((uintptr_t)kv & 15) return einval("kv_cache must be 16-byte aligned");
+  if ((uintptr_t)logits & 3) return einval("logits_out must be 4-byte aligned");
+  if (((uintptr_t)next_token & 3) || ((uintptr_t)token_dev & 3)) return einval("token buffers must be 4-byte aligned");
   if (pos < 0 || pos >= c->cfg.max_ctx) return MK_ERANGE;
   if (!token_dev && (token < 0 || token >= c->cfg.vocab)) return MK_ERANGE;
   HIPCHK(hipSetDevice(c->device));
@@ -170,6 +184,7 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
 extern "C" {
 
 int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
+  abi_enter();
   if (!cfg || !out) return MK_EINVAL;
   *out = nullptr;
   std::string why;
@@ -207,6 +222,7 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
 }
 
 int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out) {
+  abi_enter();
   if (!cfg || !out) return MK_EINVAL;
   *out = nullptr;
   mk_ctx* c = new mk_ctx();
@@ -226,6 +242,7 @@ int mk_plan_only(const mk_config* cfg, int n_cus, mk_ctx** out) {
 }
 
 int mk_load_weights(mk_ctx* c, const mk_weights* w) {
+  abi_enter();
   if (!c || !w) return MK_EINVAL;
   if (c->plan_only) return MK_ESTATE;
   const mk_config& g = c->cfg;
@@ -328,11 +345,13 @@ int mk_decode_step(mk_ctx* c, int32_t token, int32_t pos, void* kv_cache, float*
 
 int mk_decode_step_dev(mk_ctx* c, const int32_t* token_dev, int32_t pos, void* kv_cache, float* logits_out,
                        int32_t* next_token, void* stream) {
-  if (!token_dev) return MK_EINVAL;
+  abi_enter();
+  if (!token_dev) return einval("token_dev must not be null");
   return launch(c, 0, token_dev, pos, kv_cache, logits_out, next_token, (hipStream_t)stream);
 }
 
 int mk_sync(mk_ctx* c, void* stream) {
+  abi_enter();
   if (!c) return MK_EINVAL;
   if (!c->loaded) return MK_ESTATE;
   HIPCHK(hipSetDevice(c->device));
@@ -351,12 +370,14 @@ int mk_sync(mk_ctx* c, void* stream) {
 }
 
 int mk_set_watchdog_us(mk_ctx* c, int64_t us) {
+  abi_enter();
   if (!c || us < 0) return MK_EINVAL;
   c->watchdog_us = us;
   return MK_OK;
 }
 
 int mk_plan_info(const mk_ctx* c, int32_t info[8]) {
+  abi_enter();
   if (!c || !info) return MK_EINVAL;
   if (c->plan.off.empty()) return MK_ESTATE;
   info[0] = c->plan.n_cus;
@@ -371,6 +392,7 @@ int mk_plan_info(const mk_ctx* c, int32_t info[8]) {
 }
 
 int mk_plan_copy(const mk_ctx* c, int32_t* offsets, int32_t* records, int64_t cap_words) {
+  abi_enter();
   if (!c || !offsets || !records) return MK_EINVAL;
   if (c->plan.off.empty()) return MK_ESTATE;
   if (cap_words < (int64_t)c->plan.rec.size() * MK_INSTR_WORDS) return MK_EINVAL;
@@ -380,6 +402,7 @@ int mk_plan_copy(const mk_ctx* c, int32_t* offsets, int32_t* records, int64_t ca
 }
 
 int mk_debug_dump(const mk_ctx* c, uint64_t* host, int64_t cap, int64_t offsets[6]) {
+  abi_enter();
   if (!c || !offsets) return MK_EINVAL;
   if (!c->loaded) return MK_ESTATE;
   offsets[0] = (int64_t)c->off_x;
@@ -397,6 +420,7 @@ int mk_debug_dump(const mk_ctx* c, uint64_t* host, int64_t cap, int64_t offsets[
 }
 
 int mk_set_trace(mk_ctx* c, uint64_t* dev_buf, int64_t capacity_words, int64_t* required_words) {
+  abi_enter();
   if (!c) return MK_EINVAL;
   if (c->plan.off.empty()) return MK_ESTATE;
   int len = 0;

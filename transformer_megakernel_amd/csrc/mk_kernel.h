@@ -546,7 +546,9 @@ struct Waiter {
   __device__ __forceinline__ bool tick(const MkParams& p, MkShared<S>& sh, bool nosleep = false) {
     if (!nosleep) __builtin_amdgcn_s_sleep(1);
     if (lds_load(&sh.abort_flag)) return true;
-    if ((++n & 63) == 0) {
+    // A zero budget gives up at the first round of waiting (the host's way to exercise the
+    // abandon path); otherwise the clock is read every 64 rounds.
+    if ((++n & 63) == 0 || p.watchdog_ticks == 0) {
       if (global_check &&
           __hip_atomic_load(&p.ctrl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
         lds_store(&sh.abort_flag, 1);
@@ -711,17 +713,25 @@ __device__ __forceinline__ void prefetch_wave(const MkParams& p, MkShared<S>& sh
       }
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // bound the loads in flight
     }
-    trace_mark(p, i, 9, lane);
     base += d.np;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Page k for a compute wave, once it has landed (nullptr if the wait was abandoned).
+// When tracing, the ticks spent waiting are added to `waited` (the wave's total for the
+// instruction, recorded once at its end).
 template <class S>
-__device__ __forceinline__ const char* page_wait(const MkParams& p, MkShared<S>& sh, const char* ring_base, int k) {
+__device__ __forceinline__ const char* page_wait(const MkParams& p, MkShared<S>& sh, const char* ring_base, int k,
+                                                 u64& waited) {
   const int slot = k % Ring<S>::NSLOT;
-  if (!wait_flag(p, sh, &sh.full[slot], k + 1, false)) return nullptr;
+  if (p.trace && lds_load(&sh.full[slot]) < k + 1) {
+    const u64 t0 = __builtin_amdgcn_s_memrealtime();
+    if (!wait_flag(p, sh, &sh.full[slot], k + 1, false)) return nullptr;
+    waited += (u64)__builtin_amdgcn_s_memrealtime() - t0;
+  } else if (!wait_flag(p, sh, &sh.full[slot], k + 1, false)) {
+    return nullptr;
+  }
   return ring_base + slot * MK_PAGE_BYTES;
 }
 // The wave has finished reading page k: once its LDS reads have returned the loader
@@ -755,7 +765,7 @@ __device__ __forceinline__ int qkv_index(int row) {
 template <class S, int SEG>
 __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
                                      const float* act, int base, int w, int lane, uint32_t epoch, u64* best,
-                                     const uint4 (&hold)[16], int mode) {
+                                     const uint4 (&hold)[16], int mode, u64& waited) {
   using R = RowGeo<SEG>;
   // The activation slice is kept in registers for rows of up to 4 KiB; longer rows read
   // it from LDS per unit (it would otherwise take 64 registers).
@@ -846,7 +856,7 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
   }
   if (mode == 1) return true;
   for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
-    const char* page = page_wait<S>(p, sh, ring_base, base + pg);
+    const char* page = page_wait<S>(p, sh, ring_base, base + pg, waited);
     if (!page) return false;
     uint4 wv[R::USED];
 #pragma unroll
@@ -968,7 +978,7 @@ __device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, i
 template <class S>
 __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
                                          const StepGeo& g, const float* act, int base, int w, int lane,
-                                         uint32_t epoch) {
+                                         uint32_t epoch, u64& waited) {
   constexpr int HD = S::HD, HPG = S::HPG, LPP = HD / 8, NSUB = MK_NC / HPG, NSLOT = Ring<S>::NSLOT;
   // q-head mode: head d.b of the group; every wave reads every page and takes units
   // w, w + MK_NC of it.  Otherwise one head per wave (w % HPG) over pages t, t + NSUB, ...
@@ -985,7 +995,7 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
   st.l = 0.f;
   for (int pg = qh ? 0 : t; pg < d.np; pg += qh ? 1 : NSUB) {
     const int k = base + pg;
-    const char* page = page_wait<S>(p, sh, ring_base, k);
+    const char* page = page_wait<S>(p, sh, ring_base, k, waited);
     if (!page) return false;
     const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
     if (qh)
@@ -1136,16 +1146,19 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     if (w == 0) trace_mark(p, i, 5, lane);
     const float* act = sh.act[i % MK_NACT];
     bool ok = true;
+    u64 waited = 0;
     if (d.op == MK_OP_ATTN) {
-      if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch);
+      if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch, waited);
     } else if (d.op == MK_OP_O) {
-      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0);
+      ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     } else if (d.op == MK_OP_DOWN) {
-      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0);
+      ok = gemv<S, 2 * S::KC>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     } else {
-      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0);
+      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     }
     if (!ok) return;
+    if (p.trace && waited && lane == 0 && i < p.trace_len)
+      atomicAdd(p.trace + ((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + 9, waited);
     if (d.op == MK_OP_LMHEAD) {
       const u64 b = wave_max_u64(best);
       if (lane == 0) sh.amax[w] = b;
@@ -1618,7 +1631,10 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, cu = blockIdx.x;
   if (threadIdx.x == 0) {
     sh.act_seq = 0;
-    sh.abort_flag = 0;
+    // A step launched after an earlier one was abandoned (device error not yet reported
+    // and reset by the host) does nothing: the communication words and the ticket may
+    // still hold that step's partial state, and its words carry the current epoch.
+    sh.abort_flag = __hip_atomic_load(&p.ctrl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
     for (int w = 0; w < MK_NC; ++w) {
       sh.done[w] = 0;
       sh.amax[w] = 0;
@@ -1637,6 +1653,7 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
     sh.token = t;
   }
   __syncthreads();
+  if (sh.abort_flag) return;
   const uint32_t epoch = sh.epoch;
   const int o0 = ((cint_t)p.plan_off)[cu];
   const int nins = ((cint_t)p.plan_off)[cu + 1] - o0;

@@ -100,6 +100,6 @@ struct MkParams {
 // Trace slots per instruction: [0] leader starts, [1] leader starts polling its
 // inputs, [2] inputs all present, [3] slot free, [4] activation staged, [5] compute
 // wave 0 starts, [6] last compute wave done, [7] leader done (attention merge /
-// argmax), [8] leader saw every compute wave done (attention / LM head), [9] prefetch
-// wave finished touching the instruction's pages.
+// argmax), [8] leader saw every compute wave done (attention / LM head), [9] ticks the
+// compute waves waited for the instruction's pages (a sum over waves).
 #define MK_TRACE_SLOTS 10

@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
         L.mk_plan_copy.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), i64]
         L.mk_debug_dump.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), i64, ctypes.POINTER(i64)]
         L.mk_set_trace.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
+        L.mk_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
         L.mk_destroy.argtypes = [vp]
         L.mk_destroy.restype = None
         L.mk_strerror.argtypes = [ctypes.c_int]
@@ -214,3 +215,10 @@ class Megakernel:
 
 # opcode numbers of the instruction records
 OP_QKV, OP_ATTN, OP_O, OP_GATEUP, OP_DOWN, OP_LMHEAD = 1, 2, 3, 4, 5, 6
+
+
+def stream_read(buf, sink, blocks: int, unroll: int, stream=None):
+    """Launch the library's plain streaming-read kernel over the whole of ``buf`` (a
+    device tensor); ``sink``: device int32 tensor of at least ``blocks`` elements."""
+    _check(lib().mk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(blocks), int(unroll),
+                                _stream(stream)), "mk_stream_read")

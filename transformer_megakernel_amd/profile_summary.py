@@ -8,6 +8,14 @@
       HBM bytes per launch of KERNEL from one FETCH_SIZE and one WRITE_SIZE run, each scaled
       by what the same counter read for an elementwise copy of COPY_BYTES bytes.
 
+  python -m transformer_megakernel_amd.profile_summary per_op DIR OUT.json -- CMD...
+      from a kernel trace (rocprofv3 --kernel-trace --output-format csv -d DIR) of
+      bench.py --per-op-baseline: the kernels of one replayed per-operation step (those
+      between two launches of the marker kernel), their count, busy time and the gaps
+      between consecutive kernels -- the article's launch cost and memory-pipeline
+      bubbles (Megakernel article, section "Why are traditional inference methods so
+      inefficient?").
+
 The traffic file records a hash of the kernel sources; bench.py reports the figure only
 while the sources are unchanged.
 """
@@ -102,6 +110,33 @@ def cmd_traffic(workload, kernel, fdir, wdir, cfdir, cwdir, copy_bytes, out, cmd
     print(json.dumps(res, indent=1))
 
 
+def cmd_per_op(d: str, out: str, cmd: str, marker: str = "stream_read_kernel") -> None:
+    rows = _rows(_find(d, "kernel_trace.csv"))
+    ks = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows))
+    marks = [i for i, k in enumerate(ks) if marker in k[2]]
+    steps = []
+    for a, b in zip(marks, marks[1:]):
+        seg = ks[a + 1:b]
+        if not seg:
+            continue
+        busy = sum(e - s0 for s0, e, _ in seg)
+        gaps = [seg[j + 1][0] - seg[j][1] for j in range(len(seg) - 1)]
+        steps.append(dict(kernels=len(seg), span_us=(seg[-1][1] - seg[0][0]) / 1e3, busy_us=busy / 1e3,
+                          mean_gap_us=(sum(gaps) / len(gaps) / 1e3) if gaps else 0.0,
+                          max_gap_us=(max(gaps) / 1e3) if gaps else 0.0,
+                          mean_kernel_us=busy / len(seg) / 1e3))
+    if not steps:
+        raise SystemExit("no marked steps in the kernel trace")
+    med = lambda key: sorted(x[key] for x in steps)[len(steps) // 2]
+    res = dict(steps_traced=len(steps), kernels_per_step=med("kernels"), step_span_us=round(med("span_us"), 1),
+               kernel_busy_us=round(med("busy_us"), 1), mean_kernel_us=round(med("mean_kernel_us"), 2),
+               mean_gap_between_kernels_us=round(med("mean_gap_us"), 3),
+               max_gap_between_kernels_us=round(med("max_gap_us"), 3),
+               idle_fraction=round(1 - med("busy_us") / med("span_us"), 4), per_step=steps, command=cmd)
+    json.dump(res, open(out, "w"), indent=1)
+    print(json.dumps({k: v for k, v in res.items() if k != "per_step"}, indent=1))
+
+
 def main(argv):
     if "--" in argv:
         i = argv.index("--")
@@ -112,6 +147,8 @@ def main(argv):
         cmd_stats(args[1], args[2], cmd)
     elif args and args[0] == "traffic" and len(args) == 9:
         cmd_traffic(*args[1:], cmd=cmd)
+    elif args and args[0] == "per_op" and len(args) == 3:
+        cmd_per_op(args[1], args[2], cmd)
     else:
         raise SystemExit(__doc__)
 

@@ -10,7 +10,9 @@ used, random weights of the same shape stand in for them):
 
 * projection / embedding matrices: N(0, 0.02) drawn in fp32, rounded to bf16 (RNE);
 * RMSNorm gains: 1 + N(0, 0.1), rounded to bf16;
-* KV cache positions [0, ctx): N(0, 1), rounded to bf16; positions >= ctx are 0;
+* KV cache positions [0, ctx): N(0, 1), rounded to bf16; positions >= ctx hold a bf16
+  quiet NaN (0x7FC0) by default, so that a read of a slot that is not attended shows up
+  as a non-finite result instead of a small error;
 * start token: uniform in [0, vocab).
 
 Every tensor has its own generator seeded from (seed, tensor index), so tensors do
@@ -143,11 +145,13 @@ def make_weights(shape: ModelShape, seed: int = 0, device="cpu") -> Weights:
     return Weights(embed, lm_head, final_norm, **L)
 
 
-def make_kv_cache(shape: ModelShape, max_ctx: int, ctx: int, seed: int = 1, device="cpu") -> torch.Tensor:
-    """bf16 cache laid out [layer][k|v][kv_head][max_ctx][head_dim]; [0, ctx) ~ N(0,1)."""
+def make_kv_cache(shape: ModelShape, max_ctx: int, ctx: int, seed: int = 1, device="cpu",
+                  unused: float = float("nan")) -> torch.Tensor:
+    """bf16 cache laid out [layer][k|v][kv_head][max_ctx][head_dim]; [0, ctx) ~ N(0,1),
+    the slots from ctx on filled with ``unused`` (a quiet NaN unless given)."""
     dev = torch.device(device)
-    kv = torch.zeros((shape.n_layers, 2, shape.n_kv_heads, max_ctx, shape.head_dim),
-                     dtype=torch.bfloat16, device=dev)
+    kv = torch.full((shape.n_layers, 2, shape.n_kv_heads, max_ctx, shape.head_dim), unused,
+                    dtype=torch.bfloat16, device=dev)
     if ctx > 0:
         for layer in range(shape.n_layers):
             kv[layer, :, :, :ctx, :] = _normal_bf16(

@@ -1,0 +1,174 @@
+"""Time breakdown of one decode step from the kernel's per-instruction trace.
+
+The Megakernel article splits one forward into where its time goes (section
+"Megakernel: a fusion design from scratch", results paragraph): storing activations,
+waiting for consistency and loading them; RMSNorm and matrix-vector work; waiting for
+weights; synchronisation between warps; setup, parameters and page state.  This module
+gives the same split for the MI355X kernel, from the timestamps ``mk_set_trace`` records
+(100 MHz ticks, per CU and instruction: see include/mk.h), in two views:
+
+* **categories** -- each CU's span (its leader's first mark to its last) is cut into
+  the intervals where its compute waves work on an instruction and the gaps between
+  them.  Inside an instruction, the time its compute waves waited for weight pages
+  (slot 9, averaged over the waves) is *weight waits* and the rest *compute*.  A gap
+  is attributed, by the leader's marks of the next instruction, to *dependency waits*
+  (polling other CUs' results: the article's consistency waits), *activation staging*
+  (RMSNorm / RoPE / bf16 K,V and writes into LDS), *inter-wave sync* (the leader waiting
+  for the compute waves to release an activation slot), or *other* (instruction
+  decode, parameter loads, the final argmax).  The per-CU figures are averaged.
+* **critical path per layer** -- the phase boundaries of one layer: a phase starts when
+  the median CU has its inputs and ends when its slowest CU is done, because every next
+  phase reads all of its results.  Hops are the gaps between one phase's end and the
+  next one's start.
+
+Plain NumPy; it reads only the trace and the plan.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TICK_US = 0.01          # s_memrealtime runs at 100 MHz
+QKV, ATTN, O, GATEUP, DOWN, LMHEAD = 1, 2, 3, 4, 5, 6
+N_COMPUTE_WAVES = 4
+
+CATEGORIES = ("dependency waits", "activation staging", "inter-wave sync", "compute (matvec, attention)",
+              "weight waits", "other")
+
+
+def reshape(trace_words, n_cus: int) -> np.ndarray:
+    """The flat trace buffer as int64 [n_cus][instructions][10]."""
+    t = np.asarray(trace_words).astype(np.int64)
+    return t.reshape(n_cus, -1, 10)
+
+
+def _overlap(a0, a1, b0, b1):
+    return max(0, min(a1, b1) - max(a0, b0))
+
+
+def categories(tr: np.ndarray, plan: dict) -> dict:
+    """Mean per-CU split of the step span into CATEGORIES, in microseconds."""
+    off = plan["offsets"]
+    n_cus = tr.shape[0]
+    tot = {c: 0.0 for c in CATEGORIES}
+    span = 0.0
+    for cu in range(n_cus):
+        n = int(off[cu + 1] - off[cu])
+        t = tr[cu, :n]
+        start = int(t[0, 0])
+        end = int(max(t[:, 7].max(), t[:, 6].max()))
+        span += end - start
+        cur = start                                   # end of the previous compute interval
+        acc = dict.fromkeys(CATEGORIES, 0)
+        for i in range(n):
+            c0, c1 = int(t[i, 5]), int(t[i, 6])
+            if c0 == 0 or c1 == 0:
+                continue
+            gap0, gap1 = cur, max(cur, c0)
+            g = gap1 - gap0
+            dep = _overlap(gap0, gap1, t[i, 1], t[i, 2]) if t[i, 2] else 0
+            sync = _overlap(gap0, gap1, t[i, 2], t[i, 3]) if t[i, 3] else 0
+            stage = _overlap(gap0, gap1, t[i, 3], t[i, 4]) if t[i, 4] else 0
+            acc["dependency waits"] += dep
+            acc["inter-wave sync"] += sync
+            acc["activation staging"] += stage
+            acc["other"] += g - dep - sync - stage
+            busy = max(0, c1 - max(c0, cur))
+            ww = min(busy, int(t[i, 9]) // N_COMPUTE_WAVES)
+            acc["weight waits"] += ww
+            acc["compute (matvec, attention)"] += busy - ww
+            cur = max(cur, c1)
+        acc["other"] += max(0, end - cur)             # after the last instruction: argmax, epoch
+        for k in CATEGORIES:
+            tot[k] += acc[k]
+    out = {k: v / n_cus * TICK_US for k, v in tot.items()}
+    out["span (mean over CUs)"] = span / n_cus * TICK_US
+    return out
+
+
+def plan_index(plan: dict, n_instr: int) -> np.ndarray:
+    """Opcode, layer and down-chunk index of every (CU, instruction) slot of the trace:
+    int32 [3][n_cus][n_instr] (opcode 0 where a CU's list is shorter)."""
+    off, rec = plan["offsets"], plan["records"]
+    n_cus = len(off) - 1
+    idx = np.zeros((3, n_cus, n_instr), np.int32)
+    for cu in range(n_cus):
+        r = rec[int(off[cu]):int(off[cu + 1])]
+        idx[0, cu, :len(r)] = r[:, 0]
+        idx[1, cu, :len(r)] = r[:, 1]
+        idx[2, cu, :len(r)] = r[:, 6]
+    return idx
+
+
+def _marks(tr, idx, op, layer, slot, chunk=None):
+    m = (idx[0] == op) & (idx[1] == layer)
+    if chunk is not None:
+        m &= idx[2] == chunk
+    v = tr[..., slot][m]
+    return v[v > 0]
+
+
+SEGMENTS = ("QKV", "hop QKV -> attention", "attention (incl. merge)", "hop attention -> O", "O projection",
+            "hop O -> gate/up", "gate/up", "down chunks after the last gate/up", "hop down -> next layer")
+
+
+def layer_path(tr: np.ndarray, idx: np.ndarray, n_layers: int, nch: int) -> np.ndarray:
+    """Per layer, the critical-path segments of SEGMENTS in microseconds: [n_layers][9]."""
+    out = np.zeros((n_layers, len(SEGMENTS)))
+    for l in range(n_layers):
+        b = [np.median(_marks(tr, idx, QKV, l, 2)), _marks(tr, idx, QKV, l, 6).max(),
+             np.median(_marks(tr, idx, ATTN, l, 2)), _marks(tr, idx, ATTN, l, 7).max(),
+             np.median(_marks(tr, idx, O, l, 2)), _marks(tr, idx, O, l, 6).max(),
+             np.median(_marks(tr, idx, GATEUP, l, 2)), _marks(tr, idx, GATEUP, l, 6).max(),
+             _marks(tr, idx, DOWN, l, 6, chunk=nch - 1).max(),
+             np.median(_marks(tr, idx, QKV, l + 1, 2)) if l + 1 < n_layers
+             else np.median(_marks(tr, idx, LMHEAD, n_layers, 2))]
+        out[l] = np.diff(np.array(b, dtype=np.float64)) * TICK_US
+    return out
+
+
+def lm_head(tr: np.ndarray, idx: np.ndarray, n_layers: int) -> dict:
+    """LM-head phase: inputs present (median CU) to compute done, median and slowest CU."""
+    x_in = np.median(_marks(tr, idx, LMHEAD, n_layers, 2))
+    done = _marks(tr, idx, LMHEAD, n_layers, 6)
+    fin = _marks(tr, idx, LMHEAD, n_layers, 7)
+    return {"median CU done": (np.median(done) - x_in) * TICK_US, "slowest CU done": (done.max() - x_in) * TICK_US,
+            "argmax done": (fin.max() - x_in) * TICK_US}
+
+
+def step_span(tr: np.ndarray) -> float:
+    """First mark of any CU to the last mark of any CU, microseconds."""
+    first = tr[:, 0, 0][tr[:, 0, 0] > 0].min()
+    last = max(tr[:, :, 7].max(), tr[:, :, 6].max())
+    return float(last - first) * TICK_US
+
+
+def report(traces: list, plan: dict, n_layers: int, nch: int, title: str = "") -> str:
+    """Text report averaged over several traced steps (each [n_cus][instr][10])."""
+    idx = plan_index(plan, traces[0].shape[1])
+    cats = [categories(t, plan) for t in traces]
+    paths = [layer_path(t, idx, n_layers, nch) for t in traces]
+    lms = [lm_head(t, idx, n_layers) for t in traces]
+    spans = [step_span(t) for t in traces]
+    lines = []
+    if title:
+        lines.append(title)
+    lines.append(f"traced steps: {len(traces)}; step span (first to last mark) {np.mean(spans):.1f} us")
+    lines.append("")
+    lines.append("Where a CU's time goes (mean over CUs and steps; the article's categories):")
+    keys = list(CATEGORIES) + ["span (mean over CUs)"]
+    for k in keys:
+        v = np.mean([c[k] for c in cats])
+        share = v / np.mean([c["span (mean over CUs)"] for c in cats])
+        lines.append(f"  {k:32s} {v:8.1f} us  {share:6.1%}")
+    lines.append("")
+    inner = slice(2, n_layers - 2) if n_layers > 6 else slice(0, n_layers)
+    P = np.mean(paths, axis=0)
+    lines.append(f"Critical path of one layer (us; mean over layers {inner.start}..{inner.stop - 1} and steps):")
+    for j, name in enumerate(SEGMENTS):
+        lines.append(f"  {name:36s} {P[inner, j].mean():7.2f}")
+    lines.append(f"  {'layer total':36s} {P[inner].sum(axis=1).mean():7.2f}")
+    lines.append("")
+    lines.append("LM head (us after the median CU has its inputs):")
+    for k in lms[0]:
+        lines.append(f"  {k:36s} {np.mean([m[k] for m in lms]):7.2f}")
+    return "\n".join(lines)
