@@ -126,6 +126,43 @@ def read_ceiling(mib: int) -> dict:
     return res
 
 
+GEMV_VARIANTS = {0: "fp32 FMA on widened bf16 (the decode kernel)", 1: "v_dot2 bf16 pairs, activation hi+lo",
+                 2: "MFMA 16x16x32 bf16, activation hi+mid+lo", 3: "LDS reads only"}
+
+
+def gemv_page_bench(pages: int = 4000) -> dict:
+    """Per-page cost of the step's matrix-vector work on one CU (4 waves, each over its own
+    16 KiB page of 4 rows x 2048 bf16 in LDS, fp32 activation), per variant; plus each
+    variant's first-page row sums against the fp32 FMA variant's."""
+    import numpy as np
+    import torch
+
+    from transformer_megakernel_amd import mk
+    blocks = 256
+    res = {}
+    rows = {}
+    for v, name in GEMV_VARIANTS.items():
+        ticks = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda:0")
+        out = torch.zeros(blocks * 4 * 8, dtype=torch.float32, device="cuda:0")
+        for rep in range(2):   # the first launch warms the code object
+            mk.check(mk.lib().mk_bench_gemv_page(v, pages, blocks, mk.ptr(ticks), mk.ptr(out), None),
+                     "mk_bench_gemv_page")
+            torch.cuda.synchronize()
+        t = ticks.cpu().numpy() * 0.01 / pages                 # us per page per wave (100 MHz ticks)
+        rows[v] = out.cpu().numpy().reshape(blocks * 4, 8)[0, 4:8].astype(np.float64)
+        res[name] = {"us_per_page_per_wave_median": round(float(np.median(t)), 4),
+                     "us_per_page_per_wave_max": round(float(t.max()), 4)}
+    for v in (1, 2):
+        d = np.max(np.abs(rows[v] - rows[0])) / np.max(np.abs(rows[0]))
+        res[GEMV_VARIANTS[v]]["max_rel_diff_vs_fp32_fma"] = float(f"{d:.3e}")
+    fma = res[GEMV_VARIANTS[0]]["us_per_page_per_wave_median"]
+    res["page"] = "16 KiB: 4 rows x 2048 bf16; 4 compute waves per CU, 256 CUs, 4000 pages each"
+    res["stream_time_of_a_page_us"] = round(16384 * 256 / 8e12 * 1e6 / 4, 4)   # at 8 TB/s, per wave's share
+    res["fma_vs_stream"] = round(fma / res["stream_time_of_a_page_us"], 3)
+    print(json.dumps(res), flush=True)
+    return res
+
+
 def traced_breakdown(m, shape, step_fn, n_steps: int, path: str, title: str) -> None:
     """Run ``n_steps`` steps with the per-instruction trace on and write the time
     breakdown (transformer_megakernel_amd.trace_breakdown) to ``path``."""
@@ -261,6 +298,9 @@ def main():
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="MIB",
                     help="only time plain streaming kernels (the library's streaming read over a sweep of "
                          "launch shapes, torch sum, copy) over MIB MiB and exit")
+    ap.add_argument("--gemv-page-bench", action="store_true",
+                    help="only time one matrix-vector page per wave from LDS, per variant (fp32 FMA, v_dot2, "
+                         "MFMA, LDS reads alone), and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a plain copy kernel of known "
                          "size, to calibrate the HBM byte counters) and exit")
@@ -270,6 +310,9 @@ def main():
         return
     if args.read_ceiling:
         read_ceiling(args.read_ceiling)
+        return
+    if args.gemv_page_bench:
+        gemv_page_bench()
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "

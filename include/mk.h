@@ -211,6 +211,20 @@ const char* mk_strerror(int code);
  * Errors: MK_EINVAL (bad size, alignment or launch shape), MK_EHIP (launch failed). */
 int mk_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll, void* stream);
 
+/* Per-page cost of the matrix-vector work on the compute units (a measurement, not part
+ * of the decode path): `blocks` work-groups of 4 waves, each wave computing `pages` times
+ * one 16 KiB page (4 rows x 2048 bf16, the Llama-3.2-1B row) against an fp32 activation,
+ * operands already in LDS.  variant 0: fp32 FMA on the widened bf16 (the decode kernel's
+ * path); 1: v_dot2 on bf16 pairs against a two-term bf16 split of the activation; 2: the
+ * 16x16x32 bf16 matrix instruction against a three-term split; 3: the LDS reads alone.
+ * The article finds the best matrix-vector unit differs by GPU generation (section
+ * "Megakernel: a fusion design from scratch", matrix-vector paragraph).  ticks: device
+ * uint64 [blocks * 4], s_memrealtime ticks (100 MHz) per wave; out: device fp32
+ * [blocks * 4 * 8]: per wave, 4 running sums then the first page's 4 row results.
+ * Errors: MK_EINVAL (bad variant, sizes or null), MK_EHIP (launch failed). */
+int mk_bench_gemv_page(int32_t variant, int32_t pages, int32_t blocks, unsigned long long* ticks, float* out,
+                       void* stream);
+
 /* Library version string. */
 const char* mk_version(void);
 

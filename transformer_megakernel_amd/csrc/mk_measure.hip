@@ -7,12 +7,174 @@
 //    against (the pages' own bandwidth model divides a forward's bytes by the part's
 //    bandwidth: Megakernel article, section "Why are traditional inference methods so
 //    inefficient?", bandwidth paragraph).
+//  * mk_bench_gemv_page: the per-page cost of the decode step's matrix-vector work on
+//    the compute units, one variant at a time: the article finds the best unit for its
+//    matrix-vector products differs between GPU generations (section "Megakernel: a
+//    fusion design from scratch", matrix-vector paragraph), so the choice for gfx950 is
+//    measured, page by page, with the operands already in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/mk.h"
+#include "mk_kernel.h"
 
 namespace {
+
+// ---------------------------------------------------------------- GEMV page variants
+// One page = 16 KiB of bf16 weights = 4 rows of 2048 (the Llama-3.2-1B hidden width),
+// times an fp32 activation of 2048.  Each variant computes the 4 row sums; every wave of
+// the work-group walks `pages` pages of its own 16 KiB LDS region.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int PB_ROWS = 4, PB_K = 2048, PB_WAVES = 4;
+
+// Deterministic weights and activation (the page content does not matter for the timing;
+// the variants are compared with each other on it).
+__device__ __forceinline__ float pb_w(int row, int k) {
+  uint32_t h = (uint32_t)(row * 2654435761u) ^ (uint32_t)(k * 2246822519u);
+  h ^= h >> 15; h *= 2654435761u; h ^= h >> 13;
+  return ((int)(h & 1023) - 512) * (0.05f / 512.f);
+}
+__device__ __forceinline__ float pb_x(int k) { return __sinf(0.37f * k) * 1.3f + 0.01f * (k & 7); }
+__device__ __forceinline__ uint16_t pb_bf(float f) { return (uint16_t)(__float_as_uint(f) >> 16); }
+
+__device__ __forceinline__ int pb_opaque(int v) { asm volatile("" : "+v"(v)); return v; }
+
+
+// variant 0: fp32 FMA on the widened bf16 (the decode kernel's path): lane l holds 16
+// bytes of each 1 KiB unit, the activation slice in registers; unit u = row u / 4,
+// columns 512 * (u % 4) + 8 l ...
+// variant 1: v_dot2 on bf16 pairs against the activation split in two bf16 terms
+// (hi = x truncated, lo = x - hi truncated; ~2^-16 relative).
+// variant 2: the 16x16x32 bf16 matrix instruction against the activation split in three
+// bf16 terms (hi, mid, lo: fp32-exact up to the last bit): 16 instructions per page.
+// Matrix row m = 4 j + b is weight row j over columns 512 b + 32 s + (0..31) in step s;
+// matrix column n = 4 b' + t carries term t of the activation over the same columns of
+// block b' (t = 3: zero), so row j's sum is the sum of D[4 j + b][4 b + t] over b, t.
+// The page is laid out for it: unit s holds step s, lane l its row l % 16, 8 columns at
+// 8 * (l / 16), so every step reads one contiguous 1 KiB.
+// variant 3: the LDS reads of variant 0 alone.
+template <int V>
+__global__ void __launch_bounds__(256) gemv_page_kernel(int pages, unsigned long long* ticks, float* out) {
+  __shared__ __align__(16) char lds[PB_WAVES * 16384];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  char* page = lds + wave * 16384;
+  // fill this wave's page in the variant's layout
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int row, k;
+      if (V == 2) {
+        const int m = lane % 16, g = lane / 16;
+        row = m / 4;
+        k = 512 * (m % 4) + 32 * u + 8 * g + e;
+      } else {
+        row = u / 4;
+        k = 512 * (u % 4) + 8 * lane + e;
+      }
+      v[e] = pb_bf(pb_w(row, k));
+    }
+    uint4 q;
+    q.x = v[0] | ((uint32_t)v[1] << 16); q.y = v[2] | ((uint32_t)v[3] << 16);
+    q.z = v[4] | ((uint32_t)v[5] << 16); q.w = v[6] | ((uint32_t)v[7] << 16);
+    *(uint4*)(page + u * 1024 + lane * 16) = q;
+  }
+  __syncthreads();
+  float acc_out = 0.f;
+  // activation operands, kept in registers for all pages
+  float av[4][8];
+  uint32_t xhi[4][4], xlo[4][4];
+  bf16x8_t xb[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) av[c][e] = pb_x(512 * c + 8 * lane + e);
+  if (V == 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t a0 = __float_as_uint(av[c][e]), a1 = __float_as_uint(av[c][e + 1]);
+        const float r0 = av[c][e] - __uint_as_float(a0 & 0xffff0000u);
+        const float r1 = av[c][e + 1] - __uint_as_float(a1 & 0xffff0000u);
+        xhi[c][e / 2] = (a0 >> 16) | (a1 & 0xffff0000u);
+        xlo[c][e / 2] = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
+      }
+  }
+  if (V == 2) {
+    const int n = lane % 16, g = lane / 16, bb = n / 4, t = n % 4;
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = pb_x(512 * bb + 32 * st + 8 * g + e);
+        const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+        const float r1 = x - hi;
+        const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+        const float lo = r1 - mid;
+        const float term = t == 0 ? hi : t == 1 ? mid : t == 2 ? lo : 0.f;
+        xb[st][e] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(term) >> 16));
+      }
+  }
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < pages; ++it) {
+    const char* pg = page + pb_opaque(0);
+    float y = 0.f;
+    if constexpr (V == 0 || V == 1 || V == 3) {
+      float r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 w = *(const uint4*)(pg + (4 * j + c) * 1024 + lane * 16);
+          if constexpr (V == 0) {
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              a = fmaf(__uint_as_float(ws[q] << 16), av[c][2 * q], a);
+              a = fmaf(__uint_as_float(ws[q] & 0xffff0000u), av[c][2 * q + 1], a);
+            }
+          } else if constexpr (V == 1) {
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ws[q]),
+                                                  __builtin_bit_cast(bf16x2_t, xhi[c][q]), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ws[q]),
+                                                  __builtin_bit_cast(bf16x2_t, xlo[c][q]), a, false);
+            }
+          } else {
+            a += __uint_as_float(w.x ^ w.y ^ w.z ^ w.w);
+          }
+        }
+        r[j] = a;
+      }
+      // the decode kernel's per-page reduction: row j ends in the lanes of 16-lane group j
+      y = mkdev::reduce_rows<4, 64>(r, lane);
+    } else {
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const bf16x8_t a = *(const bf16x8_t*)(pg + st * 1024 + lane * 16);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[st], d, 0, 0, 0);
+      }
+      // lane l holds D[4 (l / 16) + i][l % 16]; keep i = b' = (l % 16) / 4, sum the row's 16 lanes
+      const int sel = (lane % 16) / 4;
+      const float v = sel == 0 ? d[0] : sel == 1 ? d[1] : sel == 2 ? d[2] : d[3];
+      y = mkdev::sum16(v);
+    }
+    acc_out += y;
+    if (it == 0 && (lane % 16) == 0) out[(blockIdx.x * PB_WAVES + wave) * 8 + 4 + lane / 16] = y;
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) ticks[blockIdx.x * PB_WAVES + wave] = t1 - t0;
+  if (lane < 4) out[(blockIdx.x * PB_WAVES + wave) * 8 + lane] = acc_out;
+}
 
 // Grid-stride read of n16 16-byte words, U loads in flight per lane.  The loaded bits are
 // folded into one word per thread, which is stored only if it matches a value no input
@@ -41,6 +203,20 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restric
 }  // namespace
 
 extern "C" {
+
+int mk_bench_gemv_page(int32_t variant, int32_t pages, int32_t blocks, unsigned long long* ticks, float* out,
+                       void* stream) {
+  if (!ticks || !out || pages < 1 || blocks < 1 || blocks > 4096) return MK_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  switch (variant) {
+    case 0: hipLaunchKernelGGL(gemv_page_kernel<0>, dim3(blocks), dim3(256), 0, s, pages, ticks, out); break;
+    case 1: hipLaunchKernelGGL(gemv_page_kernel<1>, dim3(blocks), dim3(256), 0, s, pages, ticks, out); break;
+    case 2: hipLaunchKernelGGL(gemv_page_kernel<2>, dim3(blocks), dim3(256), 0, s, pages, ticks, out); break;
+    case 3: hipLaunchKernelGGL(gemv_page_kernel<3>, dim3(blocks), dim3(256), 0, s, pages, ticks, out); break;
+    default: return MK_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+}
 
 int mk_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll, void* stream) {
   if (!buf || !sink || bytes < 16 || (bytes & 15) || ((uintptr_t)buf & 15) || ((uintptr_t)sink & 3) ||

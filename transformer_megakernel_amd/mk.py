@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.mk_debug_dump.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), i64, ctypes.POINTER(i64)]
         L.mk_set_trace.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
         L.mk_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
+        L.mk_bench_gemv_page.argtypes = [i32, i32, i32, vp, vp, vp]
         L.mk_destroy.argtypes = [vp]
         L.mk_destroy.restype = None
         L.mk_strerror.argtypes = [ctypes.c_int]
@@ -87,6 +88,9 @@ def _check(code: int, where: str):
         raise MkError(code, where, lib().mk_strerror(code).decode())
 
 
+check = _check
+
+
 def make_config(shape: ModelShape, max_ctx: int) -> MkConfig:
     return MkConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                     shape.ffn, shape.vocab, max_ctx, shape.rms_eps, shape.rope_theta)
@@ -94,6 +98,9 @@ def make_config(shape: ModelShape, max_ctx: int) -> MkConfig:
 
 def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
+
+
+ptr = _ptr
 
 
 def _stream(stream) -> int:

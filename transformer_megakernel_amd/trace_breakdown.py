@@ -135,6 +135,50 @@ def lm_head(tr: np.ndarray, idx: np.ndarray, n_layers: int) -> dict:
             "argmax done": (fin.max() - x_in) * TICK_US}
 
 
+def _per_cu(tr, idx, op, layer, slot, chunk=None):
+    """The mark of one phase per CU (0 where the CU has no such instruction)."""
+    m = (idx[0] == op) & (idx[1] == layer)
+    if chunk is not None:
+        m &= idx[2] == chunk
+    return np.where(m, tr[..., slot], 0).max(axis=1)
+
+
+def mlp_timeline(tr: np.ndarray, idx: np.ndarray, layers, nch: int) -> np.ndarray:
+    """Gate/up and each down chunk, in microseconds after the median CU has its gate/up
+    inputs: rows [gate/up, down 0, ...], columns (inputs present, staged, first compute
+    wave starts, last compute wave done) x (median CU, slowest CU); mean over ``layers``."""
+    rows = []
+    for l in layers:
+        t0 = np.median(_marks(tr, idx, GATEUP, l, 2))
+        tab = []
+        for op, ch in [(GATEUP, None)] + [(DOWN, c) for c in range(nch)]:
+            r = []
+            for slot in (2, 4, 5, 6):
+                v = _per_cu(tr, idx, op, l, slot, ch)
+                v = v[v > 0]
+                r += [np.median(v) - t0, v.max() - t0] if v.size else [np.nan, np.nan]
+            tab.append(r)
+        rows.append(tab)
+    return np.mean(np.array(rows, dtype=np.float64), axis=0) * TICK_US
+
+
+def slow_cus(tr: np.ndarray, idx: np.ndarray, layers, n_layers: int) -> dict:
+    """When the CUs finish gate/up (mean over ``layers``) and the LM head, relative to the
+    median CU: CUs holding an attention item vs the others, and per XCD (work-groups are
+    dealt to the eight XCDs round-robin)."""
+    n_cus = tr.shape[0]
+    att = np.array([(((idx[0][c] == ATTN) & (_per_cu(tr, idx, ATTN, 0, 2)[c] > 0)).any()) for c in range(n_cus)])
+    out = {}
+    for name, op, lay in (("gate/up done", GATEUP, layers), ("LM head done", LMHEAD, [n_layers])):
+        d = np.mean([_per_cu(tr, idx, op, l, 6) - np.median(_per_cu(tr, idx, op, l, 6)) for l in lay], axis=0)
+        d = d * TICK_US
+        out[name] = {"attention CUs (median)": float(np.median(d[att])) if att.any() else float("nan"),
+                     "other CUs (median)": float(np.median(d[~att])),
+                     "per XCD (median)": [round(float(np.median(d[x::8])), 2) for x in range(8)],
+                     "slowest CU": int(np.argmax(d)), "slowest (us after median)": float(d.max())}
+    return out
+
+
 def step_span(tr: np.ndarray) -> float:
     """First mark of any CU to the last mark of any CU, microseconds."""
     first = tr[:, 0, 0][tr[:, 0, 0] > 0].min()
@@ -171,4 +215,22 @@ def report(traces: list, plan: dict, n_layers: int, nch: int, title: str = "") -
     lines.append("LM head (us after the median CU has its inputs):")
     for k in lms[0]:
         lines.append(f"  {k:36s} {np.mean([m[k] for m in lms]):7.2f}")
+    lay = list(range(n_layers))[inner]
+    T = np.mean([mlp_timeline(t, idx, lay, nch) for t in traces], axis=0)
+    lines.append("")
+    lines.append("Gate/up and down chunks (us after the median CU has its gate/up inputs; median CU / slowest CU):")
+    lines.append(f"  {'':12s} {'inputs present':>16s} {'staged':>16s} {'compute starts':>16s} {'compute done':>16s}")
+    for r, name in enumerate(["gate/up"] + [f"down {c}" for c in range(nch)]):
+        cells = " ".join(f"{T[r, 2 * k]:7.2f} /{T[r, 2 * k + 1]:7.2f}" for k in range(4))
+        lines.append(f"  {name:12s} {cells}")
+    S = [slow_cus(t, idx, lay, n_layers) for t in traces]
+    lines.append("")
+    lines.append("Finishing order (us after the median CU; mean over steps):")
+    for k in S[0]:
+        a = np.mean([x[k]["attention CUs (median)"] for x in S])
+        o = np.mean([x[k]["other CUs (median)"] for x in S])
+        xcd = np.mean([x[k]["per XCD (median)"] for x in S], axis=0)
+        mx = np.mean([x[k]["slowest (us after median)"] for x in S])
+        lines.append(f"  {k}: attention CUs {a:+.2f}, other CUs {o:+.2f}, slowest CU {mx:+.2f}; per XCD "
+                     + " ".join(f"{v:+.2f}" for v in xcd))
     return "\n".join(lines)
