@@ -140,6 +140,23 @@ int mk_decode_step(mk_ctx* ctx, int32_t token, int32_t pos, void* kv_cache,
 int mk_decode_step_dev(mk_ctx* ctx, const int32_t* token_dev, int32_t pos, void* kv_cache,
                        float* logits_out, int32_t* next_token, void* stream);
 
+/* As mk_decode_step, for callers that cannot allocate device memory while they run
+ * steps: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It calls no hipMalloc, hipFree or other allocating routine: the step's
+ * scratch (communication words, argmax keys, control block, token sink) lives in a
+ * 16 MiB array the library holds statically on every device it runs on (set up by
+ * mk_create; held until the process ends), instead of the context's own buffers.  The
+ * context must have weights loaded (mk_load_weights allocates once, at set-up).  Shapes
+ * whose scratch exceeds 16 MiB (wider than the Llama-3.2-1B shape) are rejected with
+ * MK_EINVAL and a message giving the size needed.  Every context on one GPU shares that
+ * array and it keeps the last step's contents: calls that overlap on one GPU (from other
+ * streams or threads, or interleaved with another context's calls on another stream)
+ * race and must not be made.  A device-side failure is reported by mk_sync(ctx); the
+ * array is then re-armed (on the device, no allocation) by the next call of this entry.
+ * Errors as mk_decode_step, plus MK_ESTATE if the device's array was not set up. */
+int mk_decode_step_noalloc(mk_ctx* ctx, int32_t token, int32_t pos, void* kv_cache,
+                           float* logits_out, int32_t* next_token, void* stream);
+
 /* Wait for the context's outstanding steps on `stream` and surface device-side
  * errors: MK_ETIMEOUT (a bounded wait expired; the article's counter waits are
  * unbounded, section "Megakernel: a fusion design from scratch", counter paragraph —

@@ -1,11 +1,13 @@
 // C ABI of the decode megakernel library: context, static schedule upload, launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
-#include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -43,7 +45,16 @@ struct mk_ctx {
   int32_t* d_next = nullptr;   // argmax sink when the caller passes none
   unsigned long long* trace = nullptr;   // borrowed device buffer, or null
   int trace_len = 0;
+  bool used_static = false;              // has run steps on the device's static scratch
 };
+
+// Scratch of the allocation-free step (mk_decode_step_noalloc): the communication words,
+// argmax keys, control block and token sink, held statically on every device the library
+// runs on.  In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress (kept per device) and only that address is ever passed on.
+#define MK_STATIC_SCRATCH_BYTES (16u << 20)
+#define MK_MAX_DEVICES 64
+static __device__ __align__(256) unsigned long long scratch[MK_STATIC_SCRATCH_BYTES / 8];
 
 namespace {
 
@@ -107,6 +118,42 @@ void free_device(mk_ctx* c) {
   c->loaded = false;
 }
 
+// ---- the static scratch, per device ------------------------------------------------
+// Layout in 64-bit words: control block at 0, argmax keys at 8, the token sink after
+// them, then the communication words (at a 256-byte boundary) with the context's layout.
+std::mutex g_static_mu;
+unsigned long long* g_static_ptr[MK_MAX_DEVICES];     // device address of `scratch`
+std::atomic<bool> g_static_rearm[MK_MAX_DEVICES];      // re-arm the control block first
+constexpr size_t ST_CTRL = 0, ST_AMAX = 8;
+size_t st_next(int n_cus) { return ST_AMAX + (((size_t)n_cus + 7) & ~(size_t)7); }
+size_t st_ll(int n_cus) { return (st_next(n_cus) + 8 + 31) & ~(size_t)31; }
+
+// After an abandoned step: advance the epoch (no word that step or any earlier one wrote
+// carries the new one, whichever context wrote it) and clear the ticket and error.
+__global__ void static_rearm_kernel(MkCtrl* ctrl) {
+  ctrl->epoch = ctrl->epoch + 1u;
+  ctrl->ticket = 0u;
+  ctrl->error = 0;
+  ctrl->bad_token = 0;
+}
+
+// Once per device, with that device current (from mk_create): look up the array's device
+// address and clear it, epoch 1.
+int static_scratch_setup(int device) {
+  if (device < 0 || device >= MK_MAX_DEVICES) return MK_OK;   // such devices use no static scratch
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_ptr[device]) return MK_OK;
+  void* p = nullptr;
+  HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+  HIPCHK(hipMemset(p, 0, MK_STATIC_SCRATCH_BYTES));
+  MkCtrl ctrl{};
+  ctrl.epoch = 1;
+  HIPCHK(hipMemcpy(p, &ctrl, sizeof(ctrl), hipMemcpyHostToDevice));
+  g_static_ptr[device] = (unsigned long long*)p;
+  g_static_rearm[device] = false;
+  return MK_OK;
+}
+
 int reset_device_state(mk_ctx* c, hipStream_t s) {
   HIPCHK(hipMemsetAsync(c->d_ll, 0, c->ll_words * sizeof(unsigned long long), s));
   MkCtrl ctrl{};
@@ -118,7 +165,7 @@ int reset_device_state(mk_ctx* c, hipStream_t s) {
 }
 
 int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void* kv, float* logits,
-           int32_t* next_token, hipStream_t s) {
+           int32_t* next_token, hipStream_t s, bool use_static = false) {
   abi_enter();
   if (!c) return MK_EINVAL;
   if (!c->loaded || c->plan_only) return MK_ESTATE;
@@ -129,8 +176,27 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   if (((uintptr_t)next_token & 3) || ((uintptr_t)token_dev & 3)) return einval("token buffers must be 4-byte aligned");
   if (pos < 0 || pos >= c->cfg.max_ctx) return MK_ERANGE;
   if (!token_dev && (token < 0 || token >= c->cfg.vocab)) return MK_ERANGE;
+  unsigned long long* st = nullptr;
+  if (use_static) {
+    st = c->device < MK_MAX_DEVICES ? g_static_ptr[c->device] : nullptr;
+    if (!st) return MK_ESTATE;
+    const size_t need = (st_ll(c->plan.n_cus) + c->ll_words) * sizeof(unsigned long long);
+    if (need > MK_STATIC_SCRATCH_BYTES) {
+      snprintf(g_hip_msg, sizeof(g_hip_msg),
+               "the allocation-free step needs %zu bytes of scratch for this shape; the static scratch "
+               "holds %u bytes",
+               need, (unsigned)MK_STATIC_SCRATCH_BYTES);
+      return MK_EINVAL;
+    }
+  }
   HIPCHK(hipSetDevice(c->device));
-  if (c->needs_reset) {
+  if (use_static) {
+    if (g_static_rearm[c->device].exchange(false)) {
+      hipLaunchKernelGGL(static_rearm_kernel, dim3(1), dim3(1), 0, s, (MkCtrl*)(st + ST_CTRL));
+      HIPCHK(hipGetLastError());
+    }
+    c->used_static = true;
+  } else if (c->needs_reset) {
     int rc = reset_device_state(c, s);
     if (rc) return rc;
   }
@@ -160,9 +226,20 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   p.ll_a = c->d_ll + c->off_a;
   p.amax = c->d_amax;
   p.ctrl = c->d_ctrl;
+  p.next_token = next_token ? next_token : c->d_next;
+  if (use_static) {   // the same words, in the device's static scratch
+    unsigned long long* ll = st + st_ll(c->plan.n_cus);
+    p.ll_x = ll + c->off_x;
+    p.ll_qkv = ll + c->off_qkv;
+    p.ll_part = ll + c->off_part;
+    p.ll_o = ll + c->off_o;
+    p.ll_a = ll + c->off_a;
+    p.amax = st + ST_AMAX;
+    p.ctrl = (MkCtrl*)(st + ST_CTRL);
+    p.next_token = next_token ? next_token : (int32_t*)(st + st_next(c->plan.n_cus));
+  }
   p.kv = (uint16_t*)kv;
   p.logits = logits;
-  p.next_token = next_token ? next_token : c->d_next;
   p.token_dev = token_dev;
   p.token = token;
   p.pos = pos;
@@ -207,6 +284,12 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
   if (per_cu < 1) {
     snprintf(g_hip_msg, sizeof(g_hip_msg), "the decode kernel does not fit on a CU of device %d", hip_device);
     return MK_EHIP;
+  }
+  {   // the allocation-free step's scratch on this device, set up once
+    HIPCHK(hipSetDevice(hip_device));
+    const int rc = static_scratch_setup(hip_device);
+    HIPCHK(hipSetDevice(prev));
+    if (rc) return rc;
   }
   mk_ctx* c = new mk_ctx();
   c->cfg = *cfg;
@@ -358,15 +441,25 @@ int mk_sync(mk_ctx* c, void* stream) {
   HIPCHK(hipStreamSynchronize((hipStream_t)stream));
   MkCtrl ctrl{};
   HIPCHK(hipMemcpy(&ctrl, c->d_ctrl, sizeof(ctrl), hipMemcpyDeviceToHost));
-  if (ctrl.error != 0) {
+  int rc = MK_OK;
+  if (ctrl.error != 0 || ctrl.bad_token) {
     c->needs_reset = true;
-    return ctrl.error;
+    rc = ctrl.error != 0 ? ctrl.error : MK_ERANGE;
   }
-  if (ctrl.bad_token) {
-    c->needs_reset = true;
-    return MK_ERANGE;
+  if (c->used_static) {   // steps this context ran on the device's static scratch
+    MkCtrl sc{};
+    HIPCHK(hipMemcpy(&sc, g_static_ptr[c->device] + ST_CTRL, sizeof(sc), hipMemcpyDeviceToHost));
+    if (sc.error != 0 || sc.bad_token) {
+      g_static_rearm[c->device] = true;
+      if (rc == MK_OK) rc = sc.error != 0 ? sc.error : MK_ERANGE;
+    }
   }
-  return MK_OK;
+  return rc;
+}
+
+int mk_decode_step_noalloc(mk_ctx* c, int32_t token, int32_t pos, void* kv_cache, float* logits_out,
+                           int32_t* next_token, void* stream) {
+  return launch(c, token, nullptr, pos, kv_cache, logits_out, next_token, (hipStream_t)stream, true);
 }
 
 int mk_set_watchdog_us(mk_ctx* c, int64_t us) {

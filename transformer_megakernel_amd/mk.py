@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.mk_load_weights.argtypes = [vp, ctypes.POINTER(MkWeights)]
         L.mk_decode_step.argtypes = [vp, i32, i32, vp, vp, vp, vp]
         L.mk_decode_step_dev.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.mk_decode_step_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, vp]
         L.mk_sync.argtypes = [vp, vp]
         L.mk_set_watchdog_us.argtypes = [vp, i64]
         L.mk_plan_info.argtypes = [vp, ctypes.POINTER(i32)]
@@ -154,6 +155,11 @@ class Megakernel:
     def decode_step_dev(self, token_dev, pos: int, kv, logits, next_token=None, stream=None):
         _check(lib().mk_decode_step_dev(self._h, _ptr(token_dev), int(pos), _ptr(kv), _ptr(logits),
                                         _ptr(next_token), _stream(stream)), "mk_decode_step_dev")
+
+    def decode_step_noalloc(self, token: int, pos: int, kv, logits, next_token=None, stream=None):
+        """mk_decode_step_noalloc: the step on the device's static scratch (allocates nothing)."""
+        _check(lib().mk_decode_step_noalloc(self._h, int(token), int(pos), _ptr(kv), _ptr(logits),
+                                            _ptr(next_token), _stream(stream)), "mk_decode_step_noalloc")
 
     def sync(self, stream=None) -> int:
         """Wait for the stream; raise on a device-side error."""
