@@ -163,6 +163,51 @@ def gemv_page_bench(pages: int = 4000) -> dict:
     return res
 
 
+def poll_bench() -> dict:
+    """Dependency-poll round trip while every CU streams weights into LDS the way the
+    decode step's loaders do (0-4 pages of 16 KiB in flight per loader wave, two loaders
+    per CU), for a vector and a scalar probe; and the time for all CUs to read one 16 KiB
+    vector of 64-bit words at once against each reading its own."""
+    import numpy as np
+    import torch
+
+    from transformer_megakernel_amd import mk
+    blocks, probes, region = 256, 40, 8 << 20
+    buf = torch.ones(blocks * region // 4, dtype=torch.float32, device="cuda:0")
+    words = torch.zeros(blocks * probes * 16, dtype=torch.int64, device="cuda:0")
+    out = torch.zeros(blocks * (probes + 4), dtype=torch.int64, device="cuda:0")
+    res = {"probe": "one 64-bit word per probe, ~1 us apart; loaders: 16 x 1 KiB LDS-direct loads per page"}
+    for scalar in (0, 1):
+        for depth in (0, 1, 2, 4):
+            for _ in range(2):
+                mk.check(mk.lib().mk_bench_poll_latency(mk.ptr(buf), region, mk.ptr(words), depth, scalar, probes,
+                                                        blocks, mk.ptr(out), None), "mk_bench_poll_latency")
+                torch.cuda.synchronize()
+            o = out.cpu().numpy()
+            t = o[:blocks * probes].reshape(blocks, probes)[:, 5:] * 0.01   # us; skip the start-up probes
+            r = {"median_us": round(float(np.median(t)), 3), "p90_us": round(float(np.percentile(t, 90)), 3)}
+            if depth:
+                end = o[blocks * probes:blocks * (probes + 1)]
+                pages = o[blocks * (probes + 1):blocks * (probes + 3)].reshape(blocks, 2).sum(axis=1)
+                start = o[blocks * (probes + 3):blocks * (probes + 4)]
+                span_s = (end.max() - start.min()) * 1e-8
+                r["loaders_gb_per_s"] = round(float(pages.sum() * 16384 / span_s / 1e9), 1)
+            res[f"{'scalar' if scalar else 'vector'} probe, {2 * depth} pages in flight per CU"] = r
+    reps = 20
+    vec = torch.ones(blocks * 2048, dtype=torch.int64, device="cuda:0")
+    out2 = torch.zeros(blocks * reps, dtype=torch.int64, device="cuda:0")
+    for shared in (1, 0):
+        for _ in range(2):
+            mk.check(mk.lib().mk_bench_bcast_read(mk.ptr(vec), shared, reps, blocks, mk.ptr(out2), None),
+                     "mk_bench_bcast_read")
+            torch.cuda.synchronize()
+        t = out2.cpu().numpy().reshape(blocks, reps)[:, 2:] * 0.01
+        res[f"16 KiB read by every CU, {'the same vector' if shared else 'each its own'}"] = {
+            "median_us": round(float(np.median(t)), 3), "p90_us": round(float(np.percentile(t, 90)), 3)}
+    print(json.dumps(res), flush=True)
+    return res
+
+
 def traced_breakdown(m, shape, step_fn, n_steps: int, path: str, title: str) -> None:
     """Run ``n_steps`` steps with the per-instruction trace on and write the time
     breakdown (transformer_megakernel_amd.trace_breakdown) to ``path``."""
@@ -301,6 +346,9 @@ def main():
     ap.add_argument("--gemv-page-bench", action="store_true",
                     help="only time one matrix-vector page per wave from LDS, per variant (fp32 FMA, v_dot2, "
                          "MFMA, LDS reads alone), and exit")
+    ap.add_argument("--poll-bench", action="store_true",
+                    help="only time a dependency poll's round trip under the loaders' weight stream, and a "
+                         "16 KiB activation broadcast, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a plain copy kernel of known "
                          "size, to calibrate the HBM byte counters) and exit")
@@ -313,6 +361,9 @@ def main():
         return
     if args.gemv_page_bench:
         gemv_page_bench()
+        return
+    if args.poll_bench:
+        poll_bench()
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "

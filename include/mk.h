@@ -242,6 +242,29 @@ int mk_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t block
 int mk_bench_gemv_page(int32_t variant, int32_t pages, int32_t blocks, unsigned long long* ticks, float* out,
                        void* stream);
 
+/* Round trip of one dependency poll while the CU streams weights (a measurement, not
+ * part of the decode path): `blocks` work-groups; in each, one wave times `probes` loads
+ * of single 64-bit words (probe_words: device uint64 [blocks * probes * 16], read only;
+ * vector agent-scope loads, or scalar loads past the scalar cache when `scalar` is 1),
+ * about 1 us apart, while two waves stream the work-group's `region_bytes` slice of
+ * stream_buf (device, blocks * region_bytes bytes, read only) into LDS with 1 KiB
+ * LDS-direct loads, keeping `depth` (0-4) pages of 16 KiB in flight each — as the decode
+ * step's loaders do.  The article's consistency waits are this poll, repeated (section
+ * "Megakernel: a fusion design from scratch", counter paragraph).  out: device uint64
+ * [blocks * (probes + 4)]: ticks (100 MHz) per probe, then per work-group the time the
+ * probes ended, the pages each loader streamed (two words) and the loaders' start time,
+ * for the streaming rate at that depth.  Errors: MK_EINVAL, MK_EHIP. */
+int mk_bench_poll_latency(const void* stream_buf, int64_t region_bytes, const uint64_t* probe_words, int32_t depth,
+                          int32_t scalar, int32_t probes, int32_t blocks, unsigned long long* out, void* stream);
+
+/* Time for `blocks` single-wave work-groups to read 16 KiB of 64-bit words with
+ * agent-scope loads, `reps` times ~0.5 us apart: all the same 16 KiB (shared = 1, the
+ * decode step's activation broadcast) or each its own (shared = 0; buf then holds blocks
+ * * 16 KiB).  out: device uint64 [blocks * reps], ticks per read.  A measurement.
+ * Errors: MK_EINVAL, MK_EHIP. */
+int mk_bench_bcast_read(const uint64_t* buf, int32_t shared, int32_t reps, int32_t blocks, unsigned long long* out,
+                        void* stream);
+
 /* Library version string. */
 const char* mk_version(void);
 

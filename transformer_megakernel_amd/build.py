@@ -26,18 +26,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile csrc/mk_api.hip (kernel + C ABI + scheduler) and csrc/mk_measure.hip
-    (measurement kernels) into libmk.so; return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
+    (measurement kernels) into ``out`` (libmk.so in the package); ``defines``: extra
+    -D options (build variants for comparison); return the path."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), "-o", tmp,
+           *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -24,8 +24,8 @@ struct mk_ctx {
   bool loaded = false;
   bool needs_reset = false;
   long long watchdog_us = 2000000;
-  int pf_pages = 0;     // L2 prefetch distance beyond the LDS ring, in pages (0: off)
-  int pf_line = 128;    // bytes between prefetch touches
+  int demand_depth = 4;      // loader pages in flight per loader for staged instructions
+  bool ll_uncached = true;   // communication words in uncached memory (else cached)
   MkPlan plan;
   const void* kernel = nullptr;   // the step kernel compiled for this shape
   // borrowed weights
@@ -74,6 +74,10 @@ struct ShapeKernel {
        mkdev::Ring<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>::NSLOT * MK_PAGE_BYTES},
 const ShapeKernel kShapeKernels[] = {MK_SHAPES(MK_KERNEL_ENTRY)};
 #undef MK_KERNEL_ENTRY
+// The ring sizes the shapes were tuned with (the LDS trace and the rest of the shared
+// state leave this much of the 160 KiB).
+static_assert(mkdev::Ring<mkdev::Shape<2048, 32, 8, 64, 8192, 4>>::NSLOT == 8, "Llama-3.2-1B ring");
+static_assert(mkdev::Ring<mkdev::Shape<4096, 32, 8, 128, 14336, 4>>::NSLOT == 6, "Llama-3.1-8B ring");
 
 const ShapeKernel* shape_kernel(const mk_config& c) {
   for (const ShapeKernel& k : kShapeKernels)
@@ -102,9 +106,47 @@ int hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
+// ---- uncached arenas for the communication words ------------------------------------
+// Every word the step exchanges between CUs is stored and polled with device-scope
+// accesses, which on this part go past the XCD's L2 anyway; in uncached device memory the
+// step measured 578 against 586 us per step with the same words cached (Llama-3.2-1B
+// shape, one GPU call).  Memory of that kind is never freed once a kernel has read it (on
+// these GPUs a later allocation can then alias it wrongly): contexts take arenas from a
+// per-process pool and give them back on destroy or reload.
+struct UcArena {
+  void* p;
+  size_t bytes;
+  int device;
+  bool in_use;
+  bool uncached;
+};
+std::mutex g_uc_mu;
+std::vector<UcArena> g_uc_pool;
+
+void* uc_acquire(int device, size_t bytes, bool uncached) {
+  std::lock_guard<std::mutex> lock(g_uc_mu);
+  for (UcArena& a : g_uc_pool)
+    if (!a.in_use && a.device == device && a.bytes >= bytes && a.uncached == uncached) {
+      a.in_use = true;
+      return a.p;
+    }
+  void* p = nullptr;
+  const hipError_t e = uncached ? hipExtMallocWithFlags(&p, bytes, hipDeviceMallocUncached) : hipMalloc(&p, bytes);
+  if (e != hipSuccess) return nullptr;
+  g_uc_pool.push_back(UcArena{p, bytes, device, true, uncached});
+  return p;
+}
+
+void uc_release(void* p) {
+  std::lock_guard<std::mutex> lock(g_uc_mu);
+  for (UcArena& a : g_uc_pool)
+    if (a.p == p) a.in_use = false;
+}
+
 void free_device(mk_ctx* c) {
   if (c->plan_only) return;
-  void* ptrs[] = {c->d_layers, c->d_off, c->d_plan, c->d_rope, c->d_ll, c->d_amax, c->d_ctrl, c->d_next};
+  if (c->d_ll) uc_release(c->d_ll);
+  void* ptrs[] = {c->d_layers, c->d_off, c->d_plan, c->d_rope, c->d_amax, c->d_ctrl, c->d_next};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   c->d_layers = nullptr;
@@ -209,8 +251,7 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   p.nslot = c->plan.slots;
   p.s_max = c->plan.s_max;
   p.min_chunk = c->plan.min_chunk;
-  p.pf_pages = c->pf_pages;
-  p.pf_line = c->pf_line;
+  p.demand_depth = c->demand_depth;
   p.eps = g.rms_eps;
   p.attn_scale = (float)(1.0 / std::sqrt((double)g.head_dim));
   p.embed = c->embed;
@@ -296,10 +337,11 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
   c->device = hip_device;
   c->n_cus = prop.multiProcessorCount;
   c->kernel = kernel;
-  // Tuning overrides of the L2 prefetch: distance in pages beyond the ring (0 turns it
-  // off) and bytes between touches.
-  if (const char* e = getenv("MK_PREFETCH_PAGES")) c->pf_pages = std::max(0, std::min(64, atoi(e)));
-  if (const char* e = getenv("MK_PREFETCH_LINE")) c->pf_line = atoi(e) == 64 ? 64 : 128;
+  // Tuning overrides, for measurement: loader pages in flight per loader for staged
+  // instructions (MK_DEMAND_DEPTH, 1-4) and cached instead of uncached communication words
+  // (MK_LL_UNCACHED=0).
+  if (const char* e = getenv("MK_LL_UNCACHED")) c->ll_uncached = atoi(e) != 0;
+  if (const char* e = getenv("MK_DEMAND_DEPTH")) c->demand_depth = std::max(1, std::min(4, atoi(e)));
   *out = c;
   return MK_OK;
 }
@@ -403,9 +445,14 @@ int mk_load_weights(mk_ctx* c, const mk_weights* w) {
       (rc = alloc((void**)&c->d_off, c->plan.off.size() * sizeof(int32_t))) ||
       (rc = alloc((void**)&c->d_plan, c->plan.rec.size() * sizeof(MkInstr))) ||
       (rc = alloc((void**)&c->d_rope, rope.size() * sizeof(float))) ||
-      (rc = alloc((void**)&c->d_ll, c->ll_words * sizeof(unsigned long long))) ||
+      !(c->d_ll = (unsigned long long*)uc_acquire(c->device, c->ll_words * sizeof(unsigned long long),
+                                                  c->ll_uncached)) ||
       (rc = alloc((void**)&c->d_amax, c->plan.n_cus * sizeof(unsigned long long))) ||
       (rc = alloc((void**)&c->d_ctrl, sizeof(MkCtrl))) || (rc = alloc((void**)&c->d_next, 64))) {
+    if (!rc) {
+      snprintf(g_hip_msg, sizeof(g_hip_msg), "uncached allocation of the communication words failed");
+      rc = MK_ENOMEM;
+    }
     free_device(c);
     return rc;
   }
@@ -518,6 +565,7 @@ int mk_set_trace(mk_ctx* c, uint64_t* dev_buf, int64_t capacity_words, int64_t* 
   if (c->plan.off.empty()) return MK_ESTATE;
   int len = 0;
   for (size_t i = 0; i + 1 < c->plan.off.size(); ++i) len = std::max(len, c->plan.off[i + 1] - c->plan.off[i]);
+  len = std::min(len, MK_TRACE_MAX);   // the kernel keeps this many instructions' marks
   const int64_t need = (int64_t)c->plan.n_cus * len * MK_TRACE_SLOTS;
   if (required_words) *required_words = need;
   if (!dev_buf) {

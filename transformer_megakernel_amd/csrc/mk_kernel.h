@@ -87,7 +87,8 @@ struct __align__(16) MkShared {
   alignas(16) int done[MK_NC];              // instructions finished, per compute wave
   int full[MK_MAX_SLOTS];                   // ring slot holds page k once full == k + 1
   int freed[MK_MAX_SLOTS];                  // ring slot's page k consumed once freed == k + 1
-  uint32_t pf_sink[64];                     // landing words of the prefetch wave's loads
+  uint32_t tr[MK_TRACE_MAX][MK_TRACE_SLOTS]; // the step's trace: ticks after t0 (slot 9: a duration)
+  unsigned long long t0;                    // s_memrealtime at the work-group's start
   int act_seq;                              // instructions staged by the leader
   int abort_flag;
   uint32_t epoch;                           // tag of this step's words
@@ -308,15 +309,18 @@ __device__ __forceinline__ u64 amax_key(float v, uint32_t idx) {
   return ((u64)u << 32) | (u64)(0xffffffffu - idx);
 }
 
-__device__ __forceinline__ void trace_mark(const MkParams& p, int i, int slot, int lane) {
+// The trace is kept in LDS during the step and written out once at its end (a global
+// store per mark would queue behind the weight stream and hold up the next poll's wait).
+template <class S>
+__device__ __forceinline__ void trace_mark(const MkParams& p, MkShared<S>& sh, int i, int slot, int lane) {
   if (p.trace && lane == 0 && i < p.trace_len)
-    p.trace[((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + slot] = __builtin_amdgcn_s_memrealtime();
+    sh.tr[i][slot] = (uint32_t)(__builtin_amdgcn_s_memrealtime() - sh.t0) + 1u;   // 0: not marked
 }
 // Latest of several waves' marks.
-__device__ __forceinline__ void trace_max(const MkParams& p, int i, int slot, int lane) {
+template <class S>
+__device__ __forceinline__ void trace_max(const MkParams& p, MkShared<S>& sh, int i, int slot, int lane) {
   if (p.trace && lane == 0 && i < p.trace_len)
-    atomicMax(p.trace + ((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + slot,
-              (u64)__builtin_amdgcn_s_memrealtime());
+    atomicMax(&sh.tr[i][slot], (uint32_t)(__builtin_amdgcn_s_memrealtime() - sh.t0) + 1u);
 }
 
 // ------------------------------------------------------------------ step geometry
@@ -591,6 +595,40 @@ __device__ __forceinline__ bool wait_all_done(const MkParams& p, MkShared<S>& sh
   return true;
 }
 
+// 16 bytes from global memory, marked non-temporal (streamed weights).
+__device__ __forceinline__ uint4 ld_nt16(const char* a) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)a);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Loads gate/up page ipg of the instruction straight into registers, laid out as the
+// loaders lay a page out in LDS (unit u of the page in hold[u]).
+template <class S, int OP, int SEG>
+__device__ __forceinline__ void load_hold(const Dec& d, int ipg, int lane, uint4 (&hold)[16]) {
+  using R = RowGeo<SEG>;
+  static_assert(R::USED == 16, "held pages are whole");
+  const int rows = (OP == MK_OP_GATEUP ? 2 * d.n : d.n) - ipg * R::RPP;
+  if constexpr (R::WIDE) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = u / R::KU, c = u % R::KU;
+      const char* a = row_addr<S, OP>(d, ipg * R::RPP + (j < rows ? j : 0)) + c * 1024 + lane * 16;
+      hold[u] = ld_nt16(a);
+    }
+  } else {
+    const int jl = lane / R::LPR, cl = lane % R::LPR;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = u * R::RPU + jl;
+      const char* a = row_addr<S, OP>(d, ipg * R::RPP + (j < rows ? j : 0)) + cl * 16;
+      hold[u] = ld_nt16(a);
+    }
+  }
+}
+
+
+
 // ------------------------------------------------------------------ page ring
 // The pages of the CU's whole list, in list order, are numbered k = 0, 1, ...; page k
 // lives in ring slot k % NSLOT, is issued by loader wave k % MK_NL and consumed by
@@ -616,7 +654,8 @@ template <class S>
 __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, char* ring_base, cinstr_t list,
                                             int nins, const StepGeo& g, int l, int lane) {
   constexpr int NSLOT = Ring<S>::NSLOT;
-  constexpr int DEPTH = NSLOT / MK_NL < 4 ? NSLOT / MK_NL : 4;   // 16 loads per page, vmcnt <= 63
+  constexpr int MAXD = NSLOT / MK_NL < 4 ? NSLOT / MK_NL : 4;   // 16 loads per page, vmcnt <= 63
+  const int DEPTH = p.demand_depth < 1 ? 1 : p.demand_depth > MAXD ? MAXD : p.demand_depth;
   const uint32_t ring = lds_addr(ring_base);
   int oldest = 0, pend = 0;   // own pages issued and not yet published: oldest, then every MK_NL-th
   int base = 0;
@@ -645,8 +684,9 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
       }
       const bool demand = lds_load(&sh.act_seq) >= i + 1;
       if (!demand && k > 0) {
-        // Prefetch: own pages first (the other loader may be waiting for one), then the
-        // other loader's page k - 1 must have landed.
+        // Prefetch: own pages first (the other loader may be waiting for one), then the other
+        // loader's page k - 1 must have landed (one page in flight per CU; two per CU measured
+        // slower, 576-585 against 574 us).
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         while (pend > 0) publish_oldest();
         if (!wait_flag(p, sh, &sh.full[(k - 1) % NSLOT], k, false)) return;
@@ -664,58 +704,6 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   while (pend > 0) publish_oldest();
-}
-
-// HBM -> L2: one 4-byte load per lane into a scratch LDS word, touching 64 lines.
-__device__ __forceinline__ void touch4(const void* g, uint32_t lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(l) : "memory", "m0");
-}
-
-// Prefetch wave.  It walks the loaders' page sequence and touches every line of page k
-// once page k - NSLOT - pf_pages has been consumed, i.e. it runs pf_pages pages beyond
-// the furthest page the ring could hold, so that weight streaming from HBM continues
-// into L2 while the ring is full and the CU waits for activations; the loaders then
-// find those pages in L2.  Nothing waits for it and no result depends on it.
-template <class S>
-__device__ __forceinline__ void prefetch_wave(const MkParams& p, MkShared<S>& sh, cinstr_t list, int nins,
-                                              const StepGeo& g, int lane) {
-  constexpr int NSLOT = Ring<S>::NSLOT;
-  const int ahead = NSLOT + p.pf_pages, line = p.pf_line;
-  const uint32_t sink = lds_addr(sh.pf_sink);
-  int base = 0;
-  for (int i = 0; i < nins; ++i) {
-    const Dec d = decode<S>(p, list[i], g);
-    lane = opaque(lane);
-    for (int pg = 0; pg < d.np; ++pg) {
-      const int j = base + pg - ahead;   // page j must have been consumed first
-      if (j >= 0 && !wait_flag(p, sh, &sh.freed[j % NSLOT], j + 1, false)) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        return;
-      }
-      if (d.op == MK_OP_ATTN) {
-        constexpr int ROWB = 2 * S::HD;
-        const int q0 = d.j0 + pg * S::PPP;
-        const int bytes = min(S::PPP, d.ce - q0) * ROWB;
-        for (int o = 0; o < bytes; o += 64 * line) {
-          const int off = min(o + lane * line, bytes - 4);
-          touch4(d.m0 + (size_t)q0 * ROWB + off, sink);
-          touch4(d.m1 + (size_t)q0 * ROWB + off, sink);
-        }
-      } else {
-        const int seg = d.op == MK_OP_O ? 2 * S::NQ : d.op == MK_OP_DOWN ? 2 * S::KC : 2 * S::D;
-        const int rows = min(d.rpp, (d.op == MK_OP_GATEUP ? 2 * d.n : d.n) - (d.rp + pg) * d.rpp);
-        for (int r = 0; r < rows; ++r) {
-          const char* rb = row_ptr<S>(d, d.rp + pg, r);
-          for (int o = 0; o < seg; o += 64 * line) touch4(rb + min(o + lane * line, seg - 4), sink);
-        }
-      }
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // bound the loads in flight
-    }
-    base += d.np;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Page k for a compute wave, once it has landed (nullptr if the wait was abandoned).
@@ -790,7 +778,8 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
       for (int j = 0; j < R::RPP; ++j) {
         float a = 0.f;
 #pragma unroll
-        for (int u = 0; u < R::KU; ++u) a = dot8(wv[j * R::KU + u], av[u], a);
+        for (int u = 0; u < R::KU; ++u)
+          a = dot8(wv[j * R::KU + u], av[u], a);
         acc[j] = a;
       }
     } else if constexpr (R::WIDE) {
@@ -865,40 +854,6 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
   }
   return true;
 }
-
-// 16 bytes from global memory, marked non-temporal (streamed weights).
-__device__ __forceinline__ uint4 ld_nt16(const char* a) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)a);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Loads gate/up page ipg of the instruction straight into registers, laid out as the
-// loaders lay a page out in LDS (unit u of the page in hold[u]).
-template <class S, int OP, int SEG>
-__device__ __forceinline__ void load_hold(const Dec& d, int ipg, int lane, uint4 (&hold)[16]) {
-  using R = RowGeo<SEG>;
-  static_assert(R::USED == 16, "held pages are whole");
-  const int rows = (OP == MK_OP_GATEUP ? 2 * d.n : d.n) - ipg * R::RPP;
-  if constexpr (R::WIDE) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int j = u / R::KU, c = u % R::KU;
-      const char* a = row_addr<S, OP>(d, ipg * R::RPP + (j < rows ? j : 0)) + c * 1024 + lane * 16;
-      hold[u] = ld_nt16(a);
-    }
-  } else {
-    const int jl = lane / R::LPR, cl = lane % R::LPR;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int j = u * R::RPU + jl;
-      const char* a = row_addr<S, OP>(d, ipg * R::RPP + (j < rows ? j : 0)) + cl * 16;
-      hold[u] = ld_nt16(a);
-    }
-  }
-}
-
-
 
 template <class S>
 __device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, int h, int s) {
@@ -1143,7 +1098,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     // The last down chunk adds the partial sums of the earlier chunks, which any wave
     // may have produced: wait until every wave has finished the previous instruction.
     if (S::NCH > 1 && d.op == MK_OP_DOWN && d.a + 1 == S::NCH && !wait_all_done(p, sh, i, false)) return;
-    if (w == 0) trace_mark(p, i, 5, lane);
+    if (w == 0) trace_mark<S>(p, sh, i, 5, lane);
     const float* act = sh.act[i % MK_NACT];
     bool ok = true;
     u64 waited = 0;
@@ -1157,16 +1112,15 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
       ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     }
     if (!ok) return;
-    if (p.trace && waited && lane == 0 && i < p.trace_len)
-      atomicAdd(p.trace + ((size_t)blockIdx.x * p.trace_len + i) * MK_TRACE_SLOTS + 9, waited);
+    if (p.trace && waited && lane == 0 && i < p.trace_len) atomicAdd(&sh.tr[i][9], (uint32_t)waited);
     if (d.op == MK_OP_LMHEAD) {
       const u64 b = wave_max_u64(best);
       if (lane == 0) sh.amax[w] = b;
     }
     base += d.np;
+    trace_max<S>(p, sh, i, 6, lane);   // before the done flag: the leader writes the trace out after it
     lds_fence();
     if (lane == 0) lds_store(&sh.done[w], i + 1);
-    trace_max(p, i, 6, lane);
   }
 }
 
@@ -1244,7 +1198,7 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, c
 #pragma unroll
     for (int k = 0; k < NW; ++k) pin(gv[k]);
   }
-  trace_mark(p, i, 1, lane);
+  trace_mark<S>(p, sh, i, 1, lane);
   float* act = sh.act[i % MK_NACT];
   float ss = 0.f;
   float xv[BW];
@@ -1272,16 +1226,16 @@ __device__ __forceinline__ bool stage_norm(const MkParams& p, MkShared<S>& sh, c
       for (int k = 0; k < BW; ++k) act[(b + k) * 64 + lane] = xv[k];
     }
   }
-  trace_mark(p, i, 2, lane);
+  trace_mark<S>(p, sh, i, 2, lane);
   const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)S::D + p.eps);
   if constexpr (NW > BW) {
     lds_fence();
-    trace_mark(p, i, 3, lane);
+    trace_mark<S>(p, sh, i, 3, lane);
 #pragma unroll
     for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (act[k * 64 + lane] * rinv) * bf16f(gain[k * 64 + lane]);
   } else {
     if (!slot_free(p, sh, i)) return false;
-    trace_mark(p, i, 3, lane);
+    trace_mark<S>(p, sh, i, 3, lane);
 #pragma unroll
     for (int k = 0; k < NW; ++k) act[k * 64 + lane] = (xv[k] * rinv) * bf16f((uint16_t)gv[k]);
   }
@@ -1302,9 +1256,9 @@ __device__ __forceinline__ bool stage_raw(const MkParams& p, MkShared<S>& sh, co
   if (xrow && has_x) xr = ll_load(xrow + lane);
   if (erow && has_x) ev = bf16f(erow[lane]);
   u64 wv[NW];
-  trace_mark(p, i, 1, lane);
+  trace_mark<S>(p, sh, i, 1, lane);
   if (!poll<S, NW>(p, sh, src, wv, epoch, lane)) return false;
-  trace_mark(p, i, 2, lane);
+  trace_mark<S>(p, sh, i, 2, lane);
   if (xrow) {
     Waiter<S> wt(true);
     while (__ballot(has_x && !ll_ok(xr, epoch)) != 0) {
@@ -1313,7 +1267,7 @@ __device__ __forceinline__ bool stage_raw(const MkParams& p, MkShared<S>& sh, co
     }
   }
   if (!slot_free(p, sh, i)) return false;
-  trace_mark(p, i, 3, lane);
+  trace_mark<S>(p, sh, i, 3, lane);
   float* act = sh.act[i % MK_NACT];
 #pragma unroll
   for (int k = 0; k < NW; ++k) act[k * 64 + lane] = ll_val(wv[k]);
@@ -1336,9 +1290,9 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
   const float* cs = p.rope + (size_t)g.pos * HD + 2 * (lane & (HALF - 1));   // [half][2]
   const float c = cs[0], sn = cs[1];
   u64 wv[NW];
-  trace_mark(p, i, 1, lane);
+  trace_mark<S>(p, sh, i, 1, lane);
   if (!poll<S, NW>(p, sh, src, wv, epoch, lane)) return false;
-  trace_mark(p, i, 2, lane);
+  trace_mark<S>(p, sh, i, 2, lane);
   float v[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) v[j] = ll_val(wv[j]);
@@ -1364,7 +1318,7 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
     }
   }
   if (!slot_free(p, sh, i)) return false;
-  trace_mark(p, i, 3, lane);
+  trace_mark<S>(p, sh, i, 3, lane);
   float* act = sh.act[i % MK_NACT];
 #pragma unroll
   for (int j = 0; j < NW; ++j) act[j * 64 + lane] = v[j];
@@ -1570,7 +1524,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     const MkInstr in = list[i];
     const int l = in.layer;
     lane = opaque(lane);
-    trace_mark(p, i, 0, lane);
+    trace_mark<S>(p, sh, i, 0, lane);
     bool ok = true;
     switch (in.op) {
       case MK_OP_QKV:
@@ -1604,18 +1558,27 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     if (!ok) return;
     lds_fence();
     if (lane == 0) lds_store(&sh.act_seq, i + 1);
-    trace_mark(p, i, 4, lane);
+    trace_mark<S>(p, sh, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
       // Partials in LDS only when several waves share a head; a merge polls global words.
       if ((MK_NC > S::HPG || g.qh) && !wait_all_done(p, sh, i + 1, true)) return;
-      trace_mark(p, i, 8, lane);
+      trace_mark<S>(p, sh, i, 8, lane);
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
     } else if (in.op == MK_OP_LMHEAD) {
       if (!wait_all_done(p, sh, i + 1, true)) return;
-      trace_mark(p, i, 8, lane);
+      trace_mark<S>(p, sh, i, 8, lane);
       lm_finalize<S>(p, sh, epoch, lane);
     }
-    trace_mark(p, i, 7, lane);
+    trace_mark<S>(p, sh, i, 7, lane);
+  }
+  if (p.trace) {
+    // every compute wave has finished the last instruction (the LM head waits for them)
+    const int n = min(nins, p.trace_len);
+    u64* dst = p.trace + (size_t)blockIdx.x * p.trace_len * MK_TRACE_SLOTS;
+    for (int k = lane; k < n * MK_TRACE_SLOTS; k += 64) {
+      const uint32_t v = sh.tr[k / MK_TRACE_SLOTS][k % MK_TRACE_SLOTS];
+      dst[k] = v == 0 ? 0ull : k % MK_TRACE_SLOTS == 9 ? (u64)v : sh.t0 + v - 1u;
+    }
   }
 }
 
@@ -1629,7 +1592,11 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   __shared__ __align__(16) char ring[Ring<S>::NSLOT * MK_PAGE_BYTES];
   // the wave index is uniform per wave; saying so keeps everything derived from it scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, cu = blockIdx.x;
+  if (p.trace) {
+    for (int k = threadIdx.x; k < MK_TRACE_MAX * MK_TRACE_SLOTS; k += MK_THREADS) (&sh.tr[0][0])[k] = 0;
+  }
   if (threadIdx.x == 0) {
+    sh.t0 = __builtin_amdgcn_s_memrealtime();
     sh.act_seq = 0;
     // A step launched after an earlier one was abandoned (device error not yet reported
     // and reset by the host) does nothing: the communication words and the ticket may
@@ -1667,10 +1634,8 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   } else if (wave < MK_NC + MK_NL) {
     __builtin_amdgcn_s_setprio(2);
     loader_wave<S>(p, sh, ring, list, nins, g, wave - MK_NC, lane);
-  } else if (wave == MK_NC + MK_NL) {
+  } else {
     __builtin_amdgcn_s_setprio(3);
     leader_wave<S>(p, sh, list, nins, g, lane, epoch);
-  } else if (p.pf_pages > 0) {
-    prefetch_wave<S>(p, sh, list, nins, g, lane);
   }
 }

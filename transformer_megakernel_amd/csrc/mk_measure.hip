@@ -200,9 +200,135 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restric
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
+// ---------------------------------------------------------------- poll latency
+// The round trip of one dependency poll while the CU streams weights: wave 0 times
+// `probes` single-word loads (a vector agent-scope load, or a scalar load that bypasses
+// the scalar cache), each of a word no other probe touches, ~1 us apart; waves 1-2 stream
+// their CU's region of `stream` into a 128 KiB LDS ring with 1 KiB LDS-direct loads, the
+// way the decode kernel's loaders do, keeping `depth` pages of 16 KiB in flight each.
+__device__ __forceinline__ void pl_wait_vmcnt(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+  }
+}
+
+template <int SCALAR>
+__global__ void __launch_bounds__(192) poll_latency_kernel(const char* stream, long long region_bytes,
+                                                           const unsigned long long* words, int depth, int probes,
+                                                           unsigned long long* out) {
+  __shared__ __align__(16) char ring[8 * 16384];
+  __shared__ int stop;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) stop = 0;
+  __syncthreads();
+  if (wave == 0) {
+    unsigned long long fold = 0;
+    for (int i = 0; i < probes; ++i) {
+      for (int k = 0; k < 20; ++k) __builtin_amdgcn_s_sleep(127);   // ~1 us between probes
+      const unsigned long long* w = words + ((size_t)blockIdx.x * probes + i) * 16;   // 128 B apart
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      unsigned long long v;
+      if constexpr (SCALAR) {
+        asm volatile("s_load_dwordx2 %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(w) : "memory");
+      } else {
+        v = 0;
+        if (lane == 0) v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = __shfl(v, 0);
+      }
+      asm volatile("" ::"v"(v) : "memory");   // the stamp below waits for the probe
+      const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+      fold += v;
+      if (lane == 0) out[(size_t)blockIdx.x * probes + i] = t1 - t0;
+    }
+    if (lane == 0) {
+      if (fold == 0x5bd1e995ull) out[0] = 0;
+      __hip_atomic_store(&stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    // the span the loaders streamed over: from the first probe to now
+    if (lane == 0) out[(size_t)gridDim.x * probes + blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+  } else if (depth > 0) {
+    const int L = wave - 1;
+    const char* base = stream + (size_t)blockIdx.x * region_bytes;
+    const uint32_t ring_l = mkdev::lds_addr(ring) + L * 4 * 16384;
+    int pend = 0;
+    long long k = 0;
+    const unsigned long long t_start = __builtin_amdgcn_s_memrealtime();
+    for (;; ++k) {
+      if (__hip_atomic_load(&stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+      const char* pg = base + ((2 * k + L) * 16384) % region_bytes;
+      const uint32_t slot = ring_l + (uint32_t)(k % 4) * 16384;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) mkdev::dma16(pg + u * 1024 + lane * 16, slot + u * 1024);
+      if (++pend >= depth) {
+        pl_wait_vmcnt((depth - 1) * 16);
+        --pend;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // pages streamed and the loader's start, for the achieved rate
+    if (lane == 0) {
+      out[(size_t)gridDim.x * (probes + 1) + blockIdx.x * 2 + L] = (unsigned long long)k;
+      if (L == 0) out[(size_t)gridDim.x * (probes + 3) + blockIdx.x] = t_start;
+    }
+  }
+}
+
+// Broadcast read of a 16 KiB vector of 64-bit words by every CU at once (agent-scope loads,
+// as the decode kernel's activation polls), against each CU reading its own 16 KiB.
+template <int SHARED>
+__global__ void __launch_bounds__(64) bcast_read_kernel(const unsigned long long* buf, int reps,
+                                                        unsigned long long* out) {
+  const int lane = threadIdx.x;
+  const unsigned long long* src = SHARED ? buf : buf + (size_t)blockIdx.x * 2048;
+  unsigned long long fold = 0;
+  for (int r = 0; r < reps; ++r) {
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long w[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) w[k] = __hip_atomic_load(src + k * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) fold += w[k];
+    fold = __shfl(fold, 0);   // every load has returned
+    asm volatile("" ::"v"(fold) : "memory");
+    const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) out[(size_t)blockIdx.x * reps + r] = t1 - t0;
+    for (int k = 0; k < 10; ++k) __builtin_amdgcn_s_sleep(127);
+  }
+  if (fold == 0x5bd1e995ull && lane == 0) out[0] = 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mk_bench_poll_latency(const void* stream_buf, int64_t region_bytes, const uint64_t* probe_words, int32_t depth,
+                          int32_t scalar, int32_t probes, int32_t blocks, unsigned long long* out, void* stream) {
+  if (!stream_buf || !probe_words || !out || region_bytes < (1 << 20) || (region_bytes & 16383) || depth < 0 ||
+      depth > 4 || probes < 1 || blocks < 1 || blocks > 4096)
+    return MK_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (scalar)
+    hipLaunchKernelGGL(poll_latency_kernel<1>, dim3(blocks), dim3(192), 0, s, (const char*)stream_buf,
+                       (long long)region_bytes, (const unsigned long long*)probe_words, depth, probes, out);
+  else
+    hipLaunchKernelGGL(poll_latency_kernel<0>, dim3(blocks), dim3(192), 0, s, (const char*)stream_buf,
+                       (long long)region_bytes, (const unsigned long long*)probe_words, depth, probes, out);
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+int mk_bench_bcast_read(const uint64_t* buf, int32_t shared, int32_t reps, int32_t blocks, unsigned long long* out,
+                        void* stream) {
+  if (!buf || !out || reps < 1 || blocks < 1 || blocks > 4096) return MK_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (shared)
+    hipLaunchKernelGGL(bcast_read_kernel<1>, dim3(blocks), dim3(64), 0, s, (const unsigned long long*)buf, reps, out);
+  else
+    hipLaunchKernelGGL(bcast_read_kernel<0>, dim3(blocks), dim3(64), 0, s, (const unsigned long long*)buf, reps, out);
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+}
 
 int mk_bench_gemv_page(int32_t variant, int32_t pages, int32_t blocks, unsigned long long* ticks, float* out,
                        void* stream) {

@@ -8,12 +8,11 @@
 #include <stdint.h>
 
 // Work-group shape, one work-group per CU: MK_NC compute waves that only read LDS,
-// MK_NL loader waves that only stream pages HBM -> LDS, one leader wave that waits on
-// dependencies and stages activation vectors, and one prefetch wave that pulls the
-// pages beyond the ring into L2 while the ring is full.
+// MK_NL loader waves that only stream pages HBM -> LDS, and one leader wave that waits on
+// dependencies and stages activation vectors.
 #define MK_NC 4
 #define MK_NL 2
-#define MK_NWAVES (MK_NC + MK_NL + 2)
+#define MK_NWAVES (MK_NC + MK_NL + 1)
 #define MK_THREADS (64 * MK_NWAVES)
 #define MK_MAX_SLOTS 16
 #define MK_PAGE_BYTES 16384               // one LDS page: 16 units of 1 KiB
@@ -66,8 +65,7 @@ struct MkCtrl {
 struct MkParams {
   int32_t n_layers, V, max_ctx, n_cus;
   int32_t nslot, s_max, min_chunk;   // nslot: pages in the LDS ring
-  int32_t pf_pages;                  // L2 prefetch distance, in pages beyond the ring (0: off)
-  int32_t pf_line;                   // bytes between the prefetch wave's touches (64 or 128)
+  int32_t demand_depth;              // pages in flight per loader for an instruction already staged
   float eps, attn_scale;
   // weights (bf16)
   const uint16_t* embed;
@@ -103,3 +101,4 @@ struct MkParams {
 // argmax), [8] leader saw every compute wave done (attention / LM head), [9] ticks the
 // compute waves waited for the instruction's pages (a sum over waves).
 #define MK_TRACE_SLOTS 10
+#define MK_TRACE_MAX 272                  // instructions of a CU's list the trace covers

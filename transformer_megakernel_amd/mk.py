@@ -16,7 +16,8 @@ import numpy as np
 from .synth import ModelShape, Weights
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmk.so")
+# MK_LIBRARY may name another build of the library (e.g. one compiled with other options).
+LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(_PKG, "libmk.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "mk.h")
 
 MK_OK, MK_EINVAL, MK_ERANGE, MK_ESTATE, MK_EHIP, MK_ETIMEOUT, MK_ENOMEM = 0, -1, -2, -3, -4, -5, -6
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.mk_set_trace.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
         L.mk_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
         L.mk_bench_gemv_page.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.mk_bench_poll_latency.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp]
+        L.mk_bench_bcast_read.argtypes = [vp, i32, i32, i32, vp, vp]
         L.mk_destroy.argtypes = [vp]
         L.mk_destroy.restype = None
         L.mk_strerror.argtypes = [ctypes.c_int]

@@ -179,6 +179,35 @@ def slow_cus(tr: np.ndarray, idx: np.ndarray, layers, n_layers: int) -> dict:
     return out
 
 
+OP_ROWS = [("QKV", QKV, None), ("attention (active items)", ATTN, None), ("O projection", O, None),
+           ("gate/up", GATEUP, None), ("down 0", DOWN, 0), ("down 1", DOWN, 1), ("down 2", DOWN, 2),
+           ("down 3", DOWN, 3), ("LM head", LMHEAD, None)]
+OP_COLS = ("poll", "slot wait", "staging", "to compute", "compute", "page waits", "leader after")
+
+
+def per_op(tr: np.ndarray, idx: np.ndarray, layers, n_layers: int) -> dict:
+    """Median over CUs (and ``layers``) of each instruction type's intervals, in us: the
+    leader's poll (marks 1-2), waiting for a free activation slot (2-3), staging (3-4),
+    compute wave 0 starting after the staging (4-5), the compute waves' span (5-6), their
+    page waits (slot 9 / 4 waves) and the leader's work after staging (4 or 6 to 7: the
+    attention merge, the argmax)."""
+    out = {}
+    for name, op, ch in OP_ROWS:
+        m = idx[0] == op
+        m &= np.isin(idx[1], [n_layers] if op == LMHEAD else list(layers))
+        if ch is not None:
+            m &= idx[2] == ch
+        t = tr[m].astype(np.float64)
+        if op == ATTN:
+            t = t[t[:, 2] > 0]
+        if not len(t):
+            continue
+        cols = [t[:, 2] - t[:, 1], t[:, 3] - t[:, 2], t[:, 4] - t[:, 3], np.maximum(0, t[:, 5] - t[:, 4]),
+                t[:, 6] - t[:, 5], t[:, 9] / N_COMPUTE_WAVES, t[:, 7] - np.maximum(t[:, 4], t[:, 6] * (op in (ATTN, LMHEAD)))]
+        out[name] = [float(np.median(c)) * TICK_US for c in cols]
+    return out
+
+
 def step_span(tr: np.ndarray) -> float:
     """First mark of any CU to the last mark of any CU, microseconds."""
     first = tr[:, 0, 0][tr[:, 0, 0] > 0].min()
@@ -223,6 +252,14 @@ def report(traces: list, plan: dict, n_layers: int, nch: int, title: str = "") -
     for r, name in enumerate(["gate/up"] + [f"down {c}" for c in range(nch)]):
         cells = " ".join(f"{T[r, 2 * k]:7.2f} /{T[r, 2 * k + 1]:7.2f}" for k in range(4))
         lines.append(f"  {name:12s} {cells}")
+    O_ = [per_op(t, idx, lay, n_layers) for t in traces]
+    lines.append("")
+    lines.append("Per instruction type (us, median over CUs, mean over layers and steps):")
+    lines.append(f"  {'':26s}" + "".join(f"{c:>13s}" for c in OP_COLS))
+    for name, _, _ in OP_ROWS:
+        if name in O_[0]:
+            v = np.mean([o[name] for o in O_], axis=0)
+            lines.append(f"  {name:26s}" + "".join(f"{x:13.2f}" for x in v))
     S = [slow_cus(t, idx, lay, n_layers) for t in traces]
     lines.append("")
     lines.append("Finishing order (us after the median CU; mean over steps):")
