@@ -163,6 +163,46 @@ def gemv_page_bench(pages: int = 4000) -> dict:
     return res
 
 
+def mall_bench() -> dict:
+    """Does a buffer read moments ago come back faster (from the 256 MB memory-side cache)?
+    Streams a 192 MiB buffer cold (after reading 2 GiB of other data), right after a
+    non-temporal read of it, and right after a plain read of it; and checks whether a 2 GiB
+    non-temporal stream in between evicts it."""
+    import numpy as np
+    import torch
+
+    from transformer_megakernel_amd import mk
+    mib = 192
+    a = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda:0")
+    big = torch.ones((2048 << 20) // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+
+    def rd(t, unroll=8):
+        mk.stream_read(t, sink, 256, unroll)
+
+    def timed(t):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rd(t)
+        e1.record()
+        torch.cuda.synchronize()
+        return round(a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+    res = {}
+    for name, prep in [("cold", lambda: rd(big)), ("after a non-temporal read", lambda: (rd(big), rd(a))),
+                       ("after a plain read", lambda: (rd(big), rd(a, -8))),
+                       ("plain read, then 2 GiB non-temporal stream", lambda: (rd(big), rd(a, -8), rd(big))),
+                       ("plain read, then 2 GiB plain stream", lambda: (rd(big), rd(a, -8), rd(big, -8)))]:
+        v = []
+        for _ in range(5):
+            prep()
+            torch.cuda.synchronize()
+            v.append(timed(a))
+        res[name + " (GB/s)"] = float(np.median(v))
+    print(json.dumps(res), flush=True)
+    return res
+
+
 def poll_bench() -> dict:
     """Dependency-poll round trip while every CU streams weights into LDS the way the
     decode step's loaders do (0-4 pages of 16 KiB in flight per loader wave, two loaders
@@ -346,6 +386,8 @@ def main():
     ap.add_argument("--gemv-page-bench", action="store_true",
                     help="only time one matrix-vector page per wave from LDS, per variant (fp32 FMA, v_dot2, "
                          "MFMA, LDS reads alone), and exit")
+    ap.add_argument("--mall-bench", action="store_true",
+                    help="only measure whether a just-read buffer is re-read faster (memory-side cache), and exit")
     ap.add_argument("--poll-bench", action="store_true",
                     help="only time a dependency poll's round trip under the loaders' weight stream, and a "
                          "16 KiB activation broadcast, then exit")
@@ -364,6 +406,9 @@ def main():
         return
     if args.poll_bench:
         poll_bench()
+        return
+    if args.mall_bench:
+        mall_bench()
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "

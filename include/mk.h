@@ -223,6 +223,7 @@ const char* mk_strerror(int code);
  * is the practical HBM read ceiling the decode step's bandwidth is reported against (the
  * pages model a forward as its bytes over the part's bandwidth: Megakernel article,
  * section "Why are traditional inference methods so inefficient?", bandwidth paragraph).
+ * unroll -8: plain (cached) loads instead of non-temporal ones, 8 in flight.
  * `sink` is device uint32 [blocks], written only for an input no caller produces (it
  * keeps the loads live).  Asynchronous on `stream`; time it with events on that stream.
  * Errors: MK_EINVAL (bad size, alignment or launch shape), MK_EHIP (launch failed). */

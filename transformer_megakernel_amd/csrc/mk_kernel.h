@@ -1494,8 +1494,13 @@ __device__ __forceinline__ void lm_finalize(const MkParams& p, MkShared<S>& sh, 
   for (int w = 0; w < MK_NC; ++w) key = sh.amax[w] > key ? sh.amax[w] : key;
   uint32_t old = 0;
   if (lane == 0) {
+    // The key goes to memory (device-scope store) and has landed before the ticket counts
+    // it; the last CU reads the keys with device-scope loads after its own ticket.  No
+    // release or acquire of the XCD's L2 is needed (nothing else read in this step depends
+    // on the order), and it would write back and invalidate the whole L2.
     __hip_atomic_store(p.amax + cu, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __hip_atomic_fetch_add(&p.ctrl->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    old = __hip_atomic_fetch_add(&p.ctrl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   old = __shfl(old, 0);
   if (old != (uint32_t)(p.n_cus - 1)) return;
@@ -1513,7 +1518,8 @@ __device__ __forceinline__ void lm_finalize(const MkParams& p, MkShared<S>& sh, 
   if (lane == 0) {
     if (p.next_token) p.next_token[0] = (int32_t)(0xffffffffu - (uint32_t)best);
     __hip_atomic_store(&p.ctrl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&p.ctrl->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    // read by the next step, after the kernel boundary
+    __hip_atomic_store(&p.ctrl->epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(256) gemv_page_kernel(int pages, unsigned long
 // Grid-stride read of n16 16-byte words, U loads in flight per lane.  The loaded bits are
 // folded into one word per thread, which is stored only if it matches a value no input
 // here produces, so the loads cannot be dropped and almost nothing is written.
-template <int U>
+template <int U, bool NT = true>
 __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ src, size_t n16,
                                                           uint32_t* __restrict__ sink) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -189,7 +189,8 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restric
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     u32x4 v[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load((const u32x4*)(src + i + j * stride));
+    for (int j = 0; j < U; ++j)
+      v[j] = NT ? __builtin_nontemporal_load((const u32x4*)(src + i + j * stride)) : *(const u32x4*)(src + i + j * stride);
 #pragma unroll
     for (int j = 0; j < U; ++j) acc += v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
@@ -351,6 +352,10 @@ int mk_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t block
   const size_t n16 = (size_t)bytes / 16;
   hipStream_t s = (hipStream_t)stream;
   const uint4* src = (const uint4*)buf;
+  if (unroll == -8) {   // plain (temporal) loads, 8 in flight
+    hipLaunchKernelGGL((stream_read_kernel<8, false>), dim3(blocks), dim3(256), 0, s, src, n16, sink);
+    return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+  }
   switch (unroll) {
     case 1: hipLaunchKernelGGL(stream_read_kernel<1>, dim3(blocks), dim3(256), 0, s, src, n16, sink); break;
     case 4: hipLaunchKernelGGL(stream_read_kernel<4>, dim3(blocks), dim3(256), 0, s, src, n16, sink); break;
