@@ -567,12 +567,16 @@ struct Waiter {
   }
 };
 
-// Wait until *flag >= target (LDS).  False if abandoned.
+// Wait until *flag >= target (LDS).  False if abandoned.  No wave reads the global
+// error word here: the leader learns of other CUs' failures in its global polls (every
+// wait also has its own time budget), and a global load issued from an LDS wait queues
+// behind the CU's page loads (about 1 us), delaying the wait's end by as much when the
+// flag flips meanwhile (1.3 us per step).
 template <class S>
 __device__ __forceinline__ bool wait_flag(const MkParams& p, MkShared<S>& sh, const int* flag, int target,
                                           bool leader) {
   if (lds_load(flag) >= target) { compiler_fence(); return true; }
-  Waiter<S> wt(leader);
+  Waiter<S> wt(false);
   while (lds_load(flag) < target)
     if (wt.tick(p, sh, !leader)) return false;
   compiler_fence();

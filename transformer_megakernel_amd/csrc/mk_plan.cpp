@@ -26,6 +26,23 @@ void split(int n, int parts, int i, int* r0, int* cnt) {
   *cnt = (int)(b - a);
 }
 
+// Like split, with part i weighted 1 + skew on even XCDs (i % 8 even) and 1 - skew on
+// odd ones.
+void split_xcd(int n, int parts, int i, double skew, int* r0, int* cnt) {
+  auto edge = [&](int k) {   // rows before part k
+    double wsum = 0, wk = 0;
+    for (int j = 0; j < parts; ++j) {
+      const double wj = (j % 8) % 2 == 0 ? 1 + skew : 1 - skew;
+      if (j < k) wk += wj;
+      wsum += wj;
+    }
+    return (long)(n * wk / wsum + 0.5);
+  };
+  const long a = edge(i), b = edge(i + 1);
+  *r0 = (int)a;
+  *cnt = (int)(b - a);
+}
+
 MkInstr mk(int op, int layer) {
   MkInstr x{};
   x.op = op;
@@ -95,7 +112,10 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
     int o0, on, q0, qn, f0, fn, v0, vn;
     split(d, n_cus, cu, &o0, &on);
     split(nqkv, n_cus, cu, &q0, &qn);
-    split(c.vocab, n_cus, cu, &v0, &vn);
+    // LM-head rows: 4 % more for CUs on even XCDs, 4 % fewer on odd ones.  In every run
+    // the odd XCDs streamed their blocks a few per cent slower (they finished the LM head
+    // 2-4 us after the even ones); with this split the slowest CU finishes ~2 us earlier.
+    split_xcd(c.vocab, n_cus, cu, n_cus % 8 == 0 ? 0.04 : 0.0, &v0, &vn);
     // Gate/up features are dealt one page (fpp features) at a time, round-robin over the
     // CUs: feature page pg goes to CU pg % n_cus.  A CU's first pages then feed the first
     // down chunk, its next pages the second, and so on, so chunk k is complete once every
@@ -138,7 +158,7 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
       }
     }
     // LM-head rows: a contiguous block per CU (measured ahead of dealing rows round-robin:
-    // the last CU finished 8 us after the median CU instead of 14 us).
+    // the last CU finished 8 us after the median CU instead of 14 us), sized per XCD above.
     MkInstr lm = mk(MK_OP_LMHEAD, c.n_layers);
     lm.r0 = v0; lm.n = vn; lm.k0 = 0; lm.kn = d; lm.rs = 1;
     p.rec.push_back(lm);
