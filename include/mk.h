@@ -193,16 +193,20 @@ int mk_debug_dump(const mk_ctx* ctx, uint64_t* host, int64_t capacity_words, int
 
 /* Per-instruction timestamp trace: the MI355X form of the article's time breakdown of
  * one forward (section "Megakernel: a fusion design from scratch", results paragraph).
- * dev_buf is a borrowed device buffer of uint64 [n_cus][L][10] with L the longest per-CU
- * instruction list; *required_words receives n_cus * L * 10 (pass dev_buf NULL to query,
- * which also turns tracing off).  The buffer must be zeroed before every traced step;
+ * dev_buf is a borrowed device buffer of uint64 [n_cus][L][12] with L the longest per-CU
+ * instruction list, at most 272; *required_words receives n_cus * L * 12 (pass dev_buf
+ * NULL to query, which also turns tracing off).  The buffer must be zeroed before every traced step;
  * the step writes, per CU and instruction i, s_memrealtime ticks (100 MHz): [0] leader
  * starts i, [1] it starts polling i's inputs, [2] the inputs are all present, [3] i's
  * activation slot is free, [4] activation staged, [5] compute wave 0 starts i, [6] the
  * last compute wave finished i (a running maximum), [7] leader finished i (incl.
  * attention merge / argmax), [8] leader saw every compute wave finish i (attention and
  * LM head only), [9] ticks the compute waves spent waiting for i's weight (or cached
- * key/value) pages to land, summed over the waves (a duration, not a time stamp).
+ * key/value) pages to land, summed over the waves (a duration, not a time stamp), [10]
+ * a loader wave issued the first of i's pages that go through the LDS ring, [11] ticks
+ * the loader waves spent waiting for a ring slot with nothing of their own in flight
+ * while holding one of i's pages, summed over the two loaders (a duration: the CU's HBM
+ * stream idles then because its buffers are full).
  * Tracing changes no result.  Errors: MK_ESTATE before a schedule exists, MK_EINVAL if
  * the buffer is too small or not 8-byte aligned. */
 int mk_set_trace(mk_ctx* ctx, uint64_t* dev_buf, int64_t capacity_words, int64_t* required_words);

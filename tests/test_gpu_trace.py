@@ -47,6 +47,11 @@ def test_traced_step_is_bit_identical_and_marks_are_ordered(name, ctx):
         # instruction's activation slot (no wave starts before it) and the last wave's end
         lo = np.where(t[:, 3] > 0, t[:, 3], t[:, 5])
         assert np.all(t[:, 9] <= tb.N_COMPUTE_WAVES * (t[:, 6] - lo + 1))
+        # an instruction's first ring page is issued before its last page is consumed, and
+        # the loaders' full-ring waits (a sum over the two loaders) fit in the step
+        issued = t[:, 10] > 0
+        assert np.all(t[issued, 10] <= t[issued, 6]), cu
+        assert np.all(t[:, 11] >= 0) and t[:, 11].sum() <= tb.N_LOADERS * (t[:, 7].max() - t[0, 0] + 1)
     nch = max(int(r[7]) for r in P["records"] if r[0] == tb.DOWN)
     rep = tb.report([tr], P, shape.n_layers, nch, name)
     print(rep, flush=True)

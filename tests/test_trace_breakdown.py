@@ -16,7 +16,7 @@ def test_categories_split_a_sequential_timeline_exactly():
     s, P = _plan()
     off = P["offsets"]
     L = int(max(np.diff(off)))
-    tr = np.zeros((P["n_cus"], L, 10), np.int64)
+    tr = np.zeros((P["n_cus"], L, tb.SLOTS), np.int64)
     setup, poll, sync, stage, comp, wwait = 3, 40, 5, 12, 70, 25
     for cu in range(P["n_cus"]):
         t = 1000 + 17 * cu
@@ -47,7 +47,7 @@ def test_layer_path_recovers_the_constructed_segments():
     s, P = _plan()
     off, rec = P["offsets"], P["records"]
     L = int(max(np.diff(off)))
-    tr = np.zeros((P["n_cus"], L, 10), np.int64)
+    tr = np.zeros((P["n_cus"], L, tb.SLOTS), np.int64)
     seg = [30, 8, 45, 11, 20, 9, 60, 33, 14]          # ticks, in tb.SEGMENTS order
     nch = int(max(r[7] for r in rec if r[0] == tb.DOWN))
     layer_len = sum(seg)

@@ -28,6 +28,7 @@ struct mk_ctx {
   bool ll_uncached = true;   // communication words in uncached memory (else cached)
   MkPlan plan;
   const void* kernel = nullptr;   // the step kernel compiled for this shape
+  const void* kernel_traced = nullptr;   // the same, with the per-instruction trace
   // borrowed weights
   const uint16_t* embed = nullptr;
   const uint16_t* lm_head = nullptr;
@@ -64,11 +65,13 @@ thread_local char g_hip_msg[512] = "";
 struct ShapeKernel {
   int D, HQ, HKV, HD, F;
   const void* kernel;
+  const void* kernel_traced;   // the same step with the per-instruction trace
   int nslot;       // pages in the LDS ring
   int lds_bytes;   // LDS of one work-group
 };
 #define MK_KERNEL_ENTRY(D, HQ, HKV, HD, F, NCH)                                                    \
   {D, HQ, HKV, HD, F, (const void*)mk_step_kernel<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>,          \
+   (const void*)mk_step_kernel<mkdev::Traced<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>>,              \
    mkdev::Ring<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>::NSLOT,                                     \
    (int)sizeof(mkdev::MkShared<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>) +                          \
        mkdev::Ring<mkdev::Shape<D, HQ, HKV, HD, F, NCH>>::NSLOT * MK_PAGE_BYTES},
@@ -78,6 +81,9 @@ const ShapeKernel kShapeKernels[] = {MK_SHAPES(MK_KERNEL_ENTRY)};
 // state leave this much of the 160 KiB).
 static_assert(mkdev::Ring<mkdev::Shape<2048, 32, 8, 64, 8192, 4>>::NSLOT == 8, "Llama-3.2-1B ring");
 static_assert(mkdev::Ring<mkdev::Shape<4096, 32, 8, 128, 14336, 4>>::NSLOT == 6, "Llama-3.1-8B ring");
+// a traced step runs with the same ring as an untraced one
+static_assert(mkdev::Ring<mkdev::Traced<mkdev::Shape<2048, 32, 8, 64, 8192, 4>>>::NSLOT == 8, "traced 1B ring");
+static_assert(mkdev::Ring<mkdev::Traced<mkdev::Shape<4096, 32, 8, 128, 14336, 4>>>::NSLOT == 6, "traced 8B ring");
 
 const ShapeKernel* shape_kernel(const mk_config& c) {
   for (const ShapeKernel& k : kShapeKernels)
@@ -293,7 +299,7 @@ int launch(mk_ctx* c, int32_t token, const int32_t* token_dev, int32_t pos, void
   // exactly that many work-groups puts one on every CU; should another kernel hold some
   // CUs, the remaining work-groups start as those CUs free up.  (A cooperative launch
   // gives the same guarantee formally, but cost ~14 us more per step, measured.)
-  HIPCHK(hipLaunchKernel(c->kernel, dim3(c->plan.n_cus), dim3(MK_THREADS), args, 0, s));
+  HIPCHK(hipLaunchKernel(c->trace ? c->kernel_traced : c->kernel, dim3(c->plan.n_cus), dim3(MK_THREADS), args, 0, s));
   return MK_OK;
 }
 
@@ -316,10 +322,14 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
   hipDeviceProp_t prop;
   HIPCHK(hipGetDeviceProperties(&prop, hip_device));
   const void* kernel = shape_kernel(*cfg)->kernel;
-  int per_cu = 0, prev = 0;
+  const void* kernel_traced = shape_kernel(*cfg)->kernel_traced;
+  int per_cu = 0, per_cu_traced = 0, prev = 0;
   HIPCHK(hipGetDevice(&prev));
   HIPCHK(hipSetDevice(hip_device));
-  const hipError_t occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, MK_THREADS, 0);
+  hipError_t occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, MK_THREADS, 0);
+  if (occ == hipSuccess)
+    occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_traced, kernel_traced, MK_THREADS, 0);
+  per_cu = std::min(per_cu, per_cu_traced);
   HIPCHK(hipSetDevice(prev));
   HIPCHK(occ);
   if (per_cu < 1) {
@@ -337,6 +347,7 @@ int mk_create(const mk_config* cfg, int hip_device, mk_ctx** out) {
   c->device = hip_device;
   c->n_cus = prop.multiProcessorCount;
   c->kernel = kernel;
+  c->kernel_traced = kernel_traced;
   // Tuning overrides, for measurement: loader pages in flight per loader for staged
   // instructions (MK_DEMAND_DEPTH, 1-4) and cached instead of uncached communication words
   // (MK_LL_UNCACHED=0).

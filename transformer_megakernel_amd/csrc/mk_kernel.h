@@ -72,6 +72,14 @@ struct Shape {
   static_assert(D % 128 == 0 && NQ % 64 == 0 && KC % 64 == 0 && GRP % 64 == 0, "widths");
   static_assert(HD == 64 || HD == 128, "head_dim");
   static_assert(NCH >= 1 && NCH <= MK_MAX_NCH, "down chunks");
+  static constexpr bool TRACE = false;
+};
+// The same widths, built with the per-instruction trace (a separate kernel, so that the
+// untraced one carries no trace code: it measured 1.5-2 % slower when the loader's
+// instrumentation was merely compiled in, from instruction-cache misses).
+template <class B>
+struct Traced : B {
+  static constexpr bool TRACE = true;
 };
 
 // LDS of one work-group (the page ring is a separate array).
@@ -87,7 +95,7 @@ struct __align__(16) MkShared {
   alignas(16) int done[MK_NC];              // instructions finished, per compute wave
   int full[MK_MAX_SLOTS];                   // ring slot holds page k once full == k + 1
   int freed[MK_MAX_SLOTS];                  // ring slot's page k consumed once freed == k + 1
-  uint32_t tr[MK_TRACE_MAX][MK_TRACE_SLOTS]; // the step's trace: ticks after t0 (slot 9: a duration)
+  uint32_t tr[S::TRACE ? MK_TRACE_MAX : 1][MK_TRACE_SLOTS];   // the trace: ticks after t0 (slots 9, 11: durations)
   unsigned long long t0;                    // s_memrealtime at the work-group's start
   int act_seq;                              // instructions staged by the leader
   int abort_flag;
@@ -313,14 +321,18 @@ __device__ __forceinline__ u64 amax_key(float v, uint32_t idx) {
 // store per mark would queue behind the weight stream and hold up the next poll's wait).
 template <class S>
 __device__ __forceinline__ void trace_mark(const MkParams& p, MkShared<S>& sh, int i, int slot, int lane) {
-  if (p.trace && lane == 0 && i < p.trace_len)
-    sh.tr[i][slot] = (uint32_t)(__builtin_amdgcn_s_memrealtime() - sh.t0) + 1u;   // 0: not marked
+  if constexpr (S::TRACE) {
+    if (lane == 0 && i < p.trace_len)
+      sh.tr[i][slot] = (uint32_t)(__builtin_amdgcn_s_memrealtime() - sh.t0) + 1u;   // 0: not marked
+  }
 }
 // Latest of several waves' marks.
 template <class S>
 __device__ __forceinline__ void trace_max(const MkParams& p, MkShared<S>& sh, int i, int slot, int lane) {
-  if (p.trace && lane == 0 && i < p.trace_len)
-    atomicMax(&sh.tr[i][slot], (uint32_t)(__builtin_amdgcn_s_memrealtime() - sh.t0) + 1u);
+  if constexpr (S::TRACE) {
+    if (lane == 0 && i < p.trace_len)
+      atomicMax(&sh.tr[i][slot], (uint32_t)(__builtin_amdgcn_s_memrealtime() - sh.t0) + 1u);
+  }
 }
 
 // ------------------------------------------------------------------ step geometry
@@ -677,9 +689,16 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
       // Slot still in use: publish own pages as they land (oldest first) while waiting.
       while (lds_load(&sh.freed[slot]) < k - NSLOT + 1) {
         if (pend == 0) {
+          // nothing of this loader's in flight: the ring is full (traced: for how long)
+          u64 t_idle = 0;
+          if constexpr (S::TRACE) t_idle = __builtin_amdgcn_s_memrealtime();
           if (!wait_flag(p, sh, &sh.freed[slot], k - NSLOT + 1, false)) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // nothing may land in LDS after the wave has left
             return;
+          }
+          if constexpr (S::TRACE) {
+            if (lane == 0 && i < p.trace_len)
+              atomicAdd(&sh.tr[i][11], (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_idle));
           }
           break;
         }
@@ -695,6 +714,7 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
         while (pend > 0) publish_oldest();
         if (!wait_flag(p, sh, &sh.full[(k - 1) % NSLOT], k, false)) return;
       }
+      if (pg == 0) trace_mark<S>(p, sh, i, 10, lane);   // the instruction's first ring page
       issue_page<S>(d, d.rp + pg, ring + (uint32_t)(slot * MK_PAGE_BYTES), lane);
       if (pend == 0) oldest = k;
       ++pend;
@@ -717,7 +737,7 @@ template <class S>
 __device__ __forceinline__ const char* page_wait(const MkParams& p, MkShared<S>& sh, const char* ring_base, int k,
                                                  u64& waited) {
   const int slot = k % Ring<S>::NSLOT;
-  if (p.trace && lds_load(&sh.full[slot]) < k + 1) {
+  if (S::TRACE && lds_load(&sh.full[slot]) < k + 1) {
     const u64 t0 = __builtin_amdgcn_s_memrealtime();
     if (!wait_flag(p, sh, &sh.full[slot], k + 1, false)) return nullptr;
     waited += (u64)__builtin_amdgcn_s_memrealtime() - t0;
@@ -1116,7 +1136,9 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
       ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     }
     if (!ok) return;
-    if (p.trace && waited && lane == 0 && i < p.trace_len) atomicAdd(&sh.tr[i][9], (uint32_t)waited);
+    if constexpr (S::TRACE) {
+      if (waited && lane == 0 && i < p.trace_len) atomicAdd(&sh.tr[i][9], (uint32_t)waited);
+    }
     if (d.op == MK_OP_LMHEAD) {
       const u64 b = wave_max_u64(best);
       if (lane == 0) sh.amax[w] = b;
@@ -1581,13 +1603,14 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     }
     trace_mark<S>(p, sh, i, 7, lane);
   }
-  if (p.trace) {
+  if constexpr (S::TRACE) {
     // every compute wave has finished the last instruction (the LM head waits for them)
     const int n = min(nins, p.trace_len);
     u64* dst = p.trace + (size_t)blockIdx.x * p.trace_len * MK_TRACE_SLOTS;
     for (int k = lane; k < n * MK_TRACE_SLOTS; k += 64) {
       const uint32_t v = sh.tr[k / MK_TRACE_SLOTS][k % MK_TRACE_SLOTS];
-      dst[k] = v == 0 ? 0ull : k % MK_TRACE_SLOTS == 9 ? (u64)v : sh.t0 + v - 1u;
+      const int slot = k % MK_TRACE_SLOTS;
+      dst[k] = v == 0 ? 0ull : (slot == 9 || slot == 11) ? (u64)v : sh.t0 + v - 1u;
     }
   }
 }
@@ -1602,7 +1625,7 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   __shared__ __align__(16) char ring[Ring<S>::NSLOT * MK_PAGE_BYTES];
   // the wave index is uniform per wave; saying so keeps everything derived from it scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, cu = blockIdx.x;
-  if (p.trace) {
+  if constexpr (S::TRACE) {
     for (int k = threadIdx.x; k < MK_TRACE_MAX * MK_TRACE_SLOTS; k += MK_THREADS) (&sh.tr[0][0])[k] = 0;
   }
   if (threadIdx.x == 0) {

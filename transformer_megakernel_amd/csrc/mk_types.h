@@ -100,5 +100,5 @@ struct MkParams {
 // wave 0 starts, [6] last compute wave done, [7] leader done (attention merge /
 // argmax), [8] leader saw every compute wave done (attention / LM head), [9] ticks the
 // compute waves waited for the instruction's pages (a sum over waves).
-#define MK_TRACE_SLOTS 10
+#define MK_TRACE_SLOTS 12
 #define MK_TRACE_MAX 272                  // instructions of a CU's list the trace covers

@@ -20,6 +20,12 @@ gives the same split for the MI355X kernel, from the timestamps ``mk_set_trace``
   the median CU has its inputs and ends when its slowest CU is done, because every next
   phase reads all of its results.  Hops are the gaps between one phase's end and the
   next one's start.
+* **HBM idle per CU** -- the ticks the loader waves spent blocked on a full page ring
+  with nothing of their own in flight (slot 11, summed over the two loaders, so halved
+  here), attributed to the instruction whose page was waiting for a slot: the account of
+  when each CU's weight stream stops because its on-chip buffers are full.  With the
+  first ring page's issue time (slot 10) it also shows how far ahead of staging each
+  instruction's pages were fetched.
 
 Plain NumPy; it reads only the trace and the plan.
 """
@@ -30,15 +36,17 @@ import numpy as np
 TICK_US = 0.01          # s_memrealtime runs at 100 MHz
 QKV, ATTN, O, GATEUP, DOWN, LMHEAD = 1, 2, 3, 4, 5, 6
 N_COMPUTE_WAVES = 4
+N_LOADERS = 2
+SLOTS = 12              # marks per (CU, instruction)
 
 CATEGORIES = ("dependency waits", "activation staging", "inter-wave sync", "compute (matvec, attention)",
               "weight waits", "other")
 
 
 def reshape(trace_words, n_cus: int) -> np.ndarray:
-    """The flat trace buffer as int64 [n_cus][instructions][10]."""
+    """The flat trace buffer as int64 [n_cus][instructions][SLOTS]."""
     t = np.asarray(trace_words).astype(np.int64)
-    return t.reshape(n_cus, -1, 10)
+    return t.reshape(n_cus, -1, SLOTS)
 
 
 def _overlap(a0, a1, b0, b1):
@@ -208,6 +216,33 @@ def per_op(tr: np.ndarray, idx: np.ndarray, layers, n_layers: int) -> dict:
     return out
 
 
+def hbm_idle(tr: np.ndarray, idx: np.ndarray, layers, n_layers: int) -> dict:
+    """Per CU and layer, microseconds the CU's loaders sat blocked on a full ring with
+    nothing in flight (slot 11 / N_LOADERS), in total and by the instruction type whose
+    page was waiting; median over CUs, mean over ``layers``.  Also per instruction type,
+    how long before its staging (mark 4) the first of its ring pages was issued (mark
+    10), median over CUs and layers (negative: issued after staging)."""
+    idle = tr[..., 11].astype(np.float64) / N_LOADERS * TICK_US
+    out = {"total": [], "by type": {}, "ahead": {}}
+    names = [(n, op, ch) for n, op, ch in OP_ROWS if op != LMHEAD]
+    for l in layers:
+        m = idx[1] == l
+        out["total"].append(float(np.median(np.where(m, idle, 0).sum(axis=1))))
+    out["total"] = float(np.mean(out["total"]))
+    for name, op, ch in names:
+        m = (idx[0] == op) & np.isin(idx[1], list(layers))
+        if ch is not None:
+            m &= idx[2] == ch
+        per_cu = np.where(m, idle, 0).sum(axis=1) / max(1, len(list(layers)))
+        out["by type"][name] = float(np.median(per_cu))
+        t = tr[m].astype(np.float64)
+        t = t[(t[:, 10] > 0) & (t[:, 4] > 0)]
+        out["ahead"][name] = float(np.median(t[:, 4] - t[:, 10])) * TICK_US if len(t) else float("nan")
+    m = idx[0] == LMHEAD
+    out["by type"]["LM head"] = float(np.median(np.where(m, idle, 0).sum(axis=1)))
+    return out
+
+
 def step_span(tr: np.ndarray) -> float:
     """First mark of any CU to the last mark of any CU, microseconds."""
     first = tr[:, 0, 0][tr[:, 0, 0] > 0].min()
@@ -216,7 +251,7 @@ def step_span(tr: np.ndarray) -> float:
 
 
 def report(traces: list, plan: dict, n_layers: int, nch: int, title: str = "") -> str:
-    """Text report averaged over several traced steps (each [n_cus][instr][10])."""
+    """Text report averaged over several traced steps (each [n_cus][instr][SLOTS])."""
     idx = plan_index(plan, traces[0].shape[1])
     cats = [categories(t, plan) for t in traces]
     paths = [layer_path(t, idx, n_layers, nch) for t in traces]
@@ -260,6 +295,21 @@ def report(traces: list, plan: dict, n_layers: int, nch: int, title: str = "") -
         if name in O_[0]:
             v = np.mean([o[name] for o in O_], axis=0)
             lines.append(f"  {name:26s}" + "".join(f"{x:13.2f}" for x in v))
+    H = [hbm_idle(t, idx, lay, n_layers) for t in traces]
+    layer_us = P[inner].sum(axis=1).mean()
+    lines.append("")
+    lines.append(f"HBM idle per CU: its loaders blocked on a full page ring with nothing in flight (us per layer, "
+                 f"median CU, mean over layers {inner.start}..{inner.stop - 1} and steps):")
+    lines.append(f"  {'total':26s} {np.mean([h['total'] for h in H]):7.2f} of the layer's {layer_us:.2f}")
+    lines.append("  by the instruction whose page waited for a slot:")
+    for k in H[0]["by type"]:
+        if k == "LM head":
+            continue
+        lines.append(f"    {k:24s} {np.mean([h['by type'][k] for h in H]):7.2f}")
+    lines.append(f"  LM head (once per step)    {np.mean([h['by type']['LM head'] for h in H]):7.2f}")
+    lines.append("  first ring page issued before the instruction was staged (us, median CU):")
+    for k in H[0]["ahead"]:
+        lines.append(f"    {k:24s} {np.nanmean([h['ahead'][k] for h in H]):7.2f}")
     S = [slow_cus(t, idx, lay, n_layers) for t in traces]
     lines.append("")
     lines.append("Finishing order (us after the median CU; mean over steps):")
