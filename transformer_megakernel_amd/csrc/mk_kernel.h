@@ -561,16 +561,17 @@ struct Waiter {
   // measured faster that way; the leader's waits, which poll global memory, keep it).
   __device__ __forceinline__ bool tick(const MkParams& p, MkShared<S>& sh, bool nosleep = false) {
     if (!nosleep) __builtin_amdgcn_s_sleep(1);
-    if (lds_load(&sh.abort_flag)) return true;
+    if (__builtin_expect(lds_load(&sh.abort_flag) != 0, 0)) return true;
     // A zero budget gives up at the first round of waiting (the host's way to exercise the
-    // abandon path); otherwise the clock is read every 64 rounds.
-    if ((++n & 63) == 0 || p.watchdog_ticks == 0) {
-      if (global_check &&
-          __hip_atomic_load(&p.ctrl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+    // abandon path); otherwise the clock is read every 64 rounds.  The rare paths are
+    // marked unlikely so that the compiler lays them out away from the wait loops.
+    if (__builtin_expect((++n & 63) == 0 || p.watchdog_ticks == 0, 0)) {
+      if (__builtin_expect(global_check &&
+                           __hip_atomic_load(&p.ctrl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0, 0)) {
         lds_store(&sh.abort_flag, 1);
         return true;
       }
-      if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
+      if (__builtin_expect((long long)__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks, 0)) {
         raise_error(p, sh, MK_ETIMEOUT);
         return true;
       }
@@ -1128,6 +1129,10 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     u64 waited = 0;
     if (d.op == MK_OP_ATTN) {
       if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch, waited);
+    } else if constexpr (S::NQ == S::D && S::KC == S::D) {
+      // every matrix-vector instruction has rows of the same length: one copy of the code
+      // (the instruction cache holds the kernel's hot code better that way)
+      ok = gemv<S, 2 * S::D>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     } else if (d.op == MK_OP_O) {
       ok = gemv<S, 2 * S::NQ>(p, sh, ring_base, d, act, base, w, lane, epoch, &best, hold, 0, waited);
     } else if (d.op == MK_OP_DOWN) {
@@ -1557,35 +1562,35 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     const int l = in.layer;
     lane = opaque(lane);
     trace_mark<S>(p, sh, i, 0, lane);
+    // One call site per staging routine: each is inlined once (the instruction cache holds
+    // the kernel's hot code better than with a copy per instruction type).
     bool ok = true;
-    switch (in.op) {
-      case MK_OP_QKV:
-        ok = stage_norm<S>(p, sh, l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D,
-                           ((clayers_t)p.layers)[l].attn_norm, i, epoch, lane);
-        break;
-      case MK_OP_ATTN:
-        if (attn_active(g, in.b, S::HPG)) ok = stage_attn<S>(p, sh, in, g, i, epoch, lane);
-        break;
-      case MK_OP_O:
-        // residual: x entering the layer (the embedding row for the first layer)
-        ok = stage_raw<S, S::NQ>(p, sh, p.ll_o + (size_t)l * S::NQ, i, epoch, lane,
-                                 l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D + in.r0,
-                                 l == 0 ? p.embed + (size_t)sh.token * S::D + in.r0 : nullptr, in.n, 0);
-        break;
-      case MK_OP_GATEUP:
-        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l + 1) * S::D, ((clayers_t)p.layers)[l].mlp_norm, i,
-                           epoch, lane);
-        break;
-      case MK_OP_DOWN:
-        // the last chunk adds the residual: x after attention
-        ok = stage_raw<S, S::KC>(p, sh, p.ll_a + (size_t)l * S::F + in.k0, i, epoch, lane,
-                                 in.a + 1 == S::NCH ? p.ll_x + (size_t)(2 * l + 1) * S::D + in.r0 : nullptr, nullptr,
-                                 in.a + 1 == S::NCH ? in.n : 0, 1);
-        break;
-      default:  // MK_OP_LMHEAD (its record carries layer = n_layers: the last residual version)
-        ok = stage_norm<S>(p, sh, p.ll_x + (size_t)(2 * l) * S::D, ((clayers_t)p.layers)[l].attn_norm, i, epoch,
-                           lane);
-        break;
+    if (in.op == MK_OP_ATTN) {
+      if (attn_active(g, in.b, S::HPG)) ok = stage_attn<S>(p, sh, in, g, i, epoch, lane);
+    } else if (in.op == MK_OP_O || in.op == MK_OP_DOWN) {
+      // O: the residual is x entering the layer (the embedding row for the first layer);
+      // the last down chunk adds x after attention
+      const bool o = in.op == MK_OP_O, last = !o && in.a + 1 == S::NCH;
+      const u64* src = o ? p.ll_o + (size_t)l * S::NQ : p.ll_a + (size_t)l * S::F + in.k0;
+      const u64* xrow = o ? (l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D + in.r0)
+                          : (last ? p.ll_x + (size_t)(2 * l + 1) * S::D + in.r0 : nullptr);
+      const uint16_t* erow = o && l == 0 ? p.embed + (size_t)sh.token * S::D + in.r0 : nullptr;
+      const int xn = o || last ? in.n : 0;
+      if constexpr (S::NQ == S::KC)
+        ok = stage_raw<S, S::NQ>(p, sh, src, i, epoch, lane, xrow, erow, xn, o ? 0 : 1);
+      else if (o)
+        ok = stage_raw<S, S::NQ>(p, sh, src, i, epoch, lane, xrow, erow, xn, 0);
+      else
+        ok = stage_raw<S, S::KC>(p, sh, src, i, epoch, lane, xrow, erow, xn, 1);
+    } else {
+      // RMSNorm staging: QKV (x entering the layer, the embedding row for the first layer),
+      // gate/up (x after attention), LM head (its record carries layer = n_layers: the last
+      // residual version, and the final norm's gain)
+      const bool gu = in.op == MK_OP_GATEUP;
+      const u64* src = gu ? p.ll_x + (size_t)(2 * l + 1) * S::D
+                          : (in.op == MK_OP_QKV && l == 0 ? nullptr : p.ll_x + (size_t)(2 * l) * S::D);
+      const MkLayerPtrs& L = ((clayers_t)p.layers)[l];
+      ok = stage_norm<S>(p, sh, src, gu ? L.mlp_norm : L.attn_norm, i, epoch, lane);
     }
     if (!ok) return;
     lds_fence();
