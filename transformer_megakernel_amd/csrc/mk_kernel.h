@@ -1370,17 +1370,12 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
   const float* act = sh.act[i % MK_NACT];
   if (g.qh) {
     // q-head mode: combine the compute waves' partials of head s with the current key.
-    if (s >= HPG) return true;
+    // The current key's score is formed while the compute waves still work; the leader
+    // then waits for them (the caller does not).
+    if (s >= HPG) return wait_all_done(p, sh, i + 1, true);
     const float* pb = &sh.part[0][0][0];
     float mw[MK_NC], lw[MK_NC], ow[MK_NC][E], kn[E], vn[E];
     float sp = 0.f;
-#pragma unroll
-    for (int w = 0; w < MK_NC; ++w) {
-      mw[w] = pb[w * STRIDE];
-      lw[w] = pb[w * STRIDE + 1];
-#pragma unroll
-      for (int c = 0; c < E; ++c) ow[w][c] = pb[w * STRIDE + 2 + c * 64 + lane];
-    }
 #pragma unroll
     for (int c = 0; c < E; ++c) {
       kn[c] = act[HPG * HD + c * 64 + lane];
@@ -1388,6 +1383,15 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
       sp = fmaf(act[s * HD + c * 64 + lane], kn[c], sp);
     }
     sp = wave_sum(sp) * p.attn_scale;
+    if (!wait_all_done(p, sh, i + 1, true)) return false;
+    trace_mark<S>(p, sh, i, 8, lane);
+#pragma unroll
+    for (int w = 0; w < MK_NC; ++w) {
+      mw[w] = pb[w * STRIDE];
+      lw[w] = pb[w * STRIDE + 1];
+#pragma unroll
+      for (int c = 0; c < E; ++c) ow[w][c] = pb[w * STRIDE + 2 + c * 64 + lane];
+    }
     float M = sp;
 #pragma unroll
     for (int w = 0; w < MK_NC; ++w) M = fmaxf(M, mw[w]);
@@ -1598,8 +1602,11 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     trace_mark<S>(p, sh, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
       // Partials in LDS only when several waves share a head; a merge polls global words.
-      if ((MK_NC > S::HPG || g.qh) && !wait_all_done(p, sh, i + 1, true)) return;
-      trace_mark<S>(p, sh, i, 8, lane);
+      // (In q-head mode attn_finalize waits itself, after the current key's score.)
+      if (!g.qh) {
+        if (MK_NC > S::HPG && !wait_all_done(p, sh, i + 1, true)) return;
+        trace_mark<S>(p, sh, i, 8, lane);
+      }
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
     } else if (in.op == MK_OP_LMHEAD) {
       if (!wait_all_done(p, sh, i + 1, true)) return;
