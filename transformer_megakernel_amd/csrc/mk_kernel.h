@@ -973,6 +973,21 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
   }
   st.m = -INFINITY;
   st.l = 0.f;
+  // The page's last reader frees it.  The count's returned value is examined one page
+  // later (or after the loop), so the wave does not wait for the LDS atomic's round trip
+  // on every page; LDS operations of a wave complete in order, so the count is taken
+  // after this wave's reads of the page.
+  int prev_k = -1, prev_old = 0;
+  auto release_prev = [&]() {
+    if (prev_k >= 0) {
+      const int old = __shfl(prev_old, 0);
+      if (old == readers - 1 && lane == 0) {
+        sh.acnt[prev_k % NSLOT] = 0;
+        lds_store(&sh.freed[prev_k % NSLOT], prev_k + 1);
+      }
+      prev_k = -1;
+    }
+  };
   for (int pg = qh ? 0 : t; pg < d.np; pg += qh ? 1 : NSUB) {
     const int k = base + pg;
     const char* page = page_wait<S>(p, sh, ring_base, k, waited);
@@ -982,16 +997,13 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
       head_page<HD, MK_NC>(st, page, npos, p.attn_scale, lane, w);
     else
       head_page<HD, 1>(st, page, npos, p.attn_scale, lane, 0);
-    lds_fence();
-    // the page's last reader frees it
+    release_prev();
     int old = 0;
     if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
-    old = __shfl(old, 0);
-    if (old == readers - 1 && lane == 0) {
-      sh.acnt[k % NSLOT] = 0;
-      lds_store(&sh.freed[k % NSLOT], k + 1);
-    }
+    prev_k = k;
+    prev_old = old;
   }
+  release_prev();
   // Sum over the lanes holding other positions (same dims): xor LPP .. 32.
 #pragma unroll
   for (int off = LPP; off < 64; off <<= 1) {
