@@ -102,6 +102,21 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
         assert items == [(g, t) for g in range(s.n_kv_heads) for t in range(P["s_max"])]
     lm = sorted((r0, n) for r0, n, *_ in cover[(OPS["LMHEAD"], s.n_layers, 0)])
     assert sum(n for _, n in lm) == s.vocab and len(lm) == n_cus
+    pos = 0
+    for r0, n in lm:   # contiguous blocks, no gaps or overlaps
+        assert r0 == pos and n > 0
+        pos += n
+    # LM-head blocks are sized per XCD (work-groups are dealt to the 8 XCDs round-robin):
+    # CUs on even XCDs get a few per cent more rows than those on odd ones
+    per_cu = [int(rec[off[cu + 1] - 1][3]) for cu in range(n_cus)]
+    if n_cus % 8 == 0:
+        even = np.mean([per_cu[c] for c in range(n_cus) if c % 2 == 0])
+        odd = np.mean([per_cu[c] for c in range(n_cus) if c % 2 == 1])
+        assert even >= odd
+        if s.vocab >= 100 * n_cus:   # rounding aside: 1.04 / 0.96
+            assert 1.07 < even / odd < 1.10
+    else:
+        assert max(per_cu) - min(per_cu) <= 1
     assert P["lds_bytes"] <= 160 * 1024
     assert P["page_bytes"] * P["ring_pages"] <= 128 * 1024
 
