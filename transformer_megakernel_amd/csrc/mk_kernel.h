@@ -794,6 +794,65 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
   }
   const int rows_total = d.op == MK_OP_GATEUP ? 2 * d.n : d.n;
   const int l = d.layer;
+  // Output row pr of the instruction (not gate/up), value v: store it (with the residual
+  // or the earlier chunks' partial sums where the instruction has them).
+  auto emit_row = [&](float v, int pr) {
+    const int gr = d.r0 + pr * d.rs;
+    if (d.op == MK_OP_QKV) {
+      ll_store(p.ll_qkv + (size_t)l * S::NQKV + qkv_index<S>(gr), v, epoch);
+    } else if (d.op == MK_OP_O) {
+      ll_store(p.ll_x + (size_t)(2 * l + 1) * S::D + gr, sh.xres[0][pr] + v, epoch);
+    } else if (d.op == MK_OP_DOWN) {
+      if (d.a + 1 < S::NCH) {
+        sh.dpart[d.a][pr] = v;
+      } else {
+        float acc2 = 0.f;
+#pragma unroll
+        for (int c = 0; c + 1 < S::NCH; ++c) acc2 += sh.dpart[c][pr];
+        ll_store(p.ll_x + (size_t)(2 * l + 2) * S::D + gr, sh.xres[1][pr] + (acc2 + v), epoch);
+      }
+    } else {   // MK_OP_LMHEAD
+      p.logits[gr] = v;
+      const u64 key = amax_key(v, (uint32_t)gr);
+      if (key > *best) *best = key;
+    }
+  };
+  // Two ring pages and four compute waves (the O projection, the first down chunks): each
+  // page is shared by two waves, one per pair of its rows, halving the time the
+  // instruction spends on its critical path.
+  if constexpr (MK_SPLIT_PAGES && AREG && R::WIDE && R::RPP == 4 && MK_NC == 4) {
+    if ((d.op == MK_OP_O || d.op == MK_OP_DOWN) && d.np == 2 && d.rp == 0 && mode == 0) {
+      constexpr int NSLOT = Ring<S>::NSLOT;
+      const int pgi = w >> 1, h = w & 1, k = base + pgi;
+      const char* page = page_wait<S>(p, sh, ring_base, k, waited);
+      if (!page) return false;
+      uint4 wv[2 * R::KU];
+#pragma unroll
+      for (int u = 0; u < 2 * R::KU; ++u) wv[u] = *(const uint4*)(page + (2 * h * R::KU + u) * 1024 + lane * 16);
+      float acc[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < R::KU; ++u) a = dot8(wv[jj * R::KU + u], av[u], a);
+        acc[jj] = a;
+      }
+      // the page's second reader frees it (the count is taken once this wave's reads of
+      // the page have returned)
+      lds_fence();
+      int old = 0;
+      if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
+      const float v = reduce_rows<2, 64>(acc, lane);
+      old = __shfl(old, 0);
+      if (old == 1 && lane == 0) {
+        sh.acnt[k % NSLOT] = 0;
+        lds_store(&sh.freed[k % NSLOT], k + 1);
+      }
+      const int pr = pgi * d.rpp + 2 * h + (lane >> 5);
+      if ((lane & 31) == 0 && pr < rows_total) emit_row(v, pr);
+      return true;
+    }
+  }
   // One page: wv holds its units; ipg is its page in the instruction; kfree the ring page
   // to release once read (-1: a page held in registers).
   auto page_body = [&](const uint4 (&wv)[R::USED], int ipg, int kfree) {
@@ -842,25 +901,7 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
         ll_store(p.ll_a + (size_t)l * S::F + gu_feature<S>(d, pr >> 1), a, epoch);
       }
     } else if (valid) {
-      const int gr = d.r0 + pr * d.rs;
-      if (d.op == MK_OP_QKV) {
-        ll_store(p.ll_qkv + (size_t)l * S::NQKV + qkv_index<S>(gr), v, epoch);
-      } else if (d.op == MK_OP_O) {
-        ll_store(p.ll_x + (size_t)(2 * l + 1) * S::D + gr, sh.xres[0][pr] + v, epoch);
-      } else if (d.op == MK_OP_DOWN) {
-        if (d.a + 1 < S::NCH) {
-          sh.dpart[d.a][pr] = v;
-        } else {
-          float acc2 = 0.f;
-#pragma unroll
-          for (int c = 0; c + 1 < S::NCH; ++c) acc2 += sh.dpart[c][pr];
-          ll_store(p.ll_x + (size_t)(2 * l + 2) * S::D + gr, sh.xres[1][pr] + (acc2 + v), epoch);
-        }
-      } else {   // MK_OP_LMHEAD
-        p.logits[gr] = v;
-        const u64 key = amax_key(v, (uint32_t)gr);
-        if (key > *best) *best = key;
-      }
+      emit_row(v, pr);
     }
   };
   // mode 0: the held page (if this wave holds one) and the ring pages; 1: only the held

@@ -22,6 +22,9 @@
 #endif
 #define MK_MAX_RES_ROWS 64                // rows of x one CU owns in a residual op
 #define MK_MAX_NCH 4                      // K-chunks of the down projection
+#ifndef MK_SPLIT_PAGES
+#define MK_SPLIT_PAGES 1                  // two-page O / down instructions: two waves per page
+#endif
 
 // Instruction opcodes — the article's six fused instructions.
 enum {

@@ -309,7 +309,9 @@ def report(traces: list, plan: dict, n_layers: int, nch: int, title: str = "") -
     lines.append(f"  LM head (once per step)    {np.mean([h['by type']['LM head'] for h in H]):7.2f}")
     lines.append("  first ring page issued before the instruction was staged (us, median CU):")
     for k in H[0]["ahead"]:
-        lines.append(f"    {k:24s} {np.nanmean([h['ahead'][k] for h in H]):7.2f}")
+        a = np.array([h["ahead"][k] for h in H], dtype=float)
+        a = a[~np.isnan(a)]
+        lines.append(f"    {k:24s} " + (f"{a.mean():7.2f}" if a.size else "      -"))
     S = [slow_cus(t, idx, lay, n_layers) for t in traces]
     lines.append("")
     lines.append("Finishing order (us after the median CU; mean over steps):")
