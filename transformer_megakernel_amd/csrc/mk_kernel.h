@@ -944,30 +944,38 @@ struct HeadState {
 // so all key and value units are read unconditionally and positions past npos only get
 // a zero weight: no branches, and the value reads overlap the score arithmetic.
 //
-// The wave takes units u0, u0 + USTEP, ... of the page (USTEP = 1: all of them).
-template <int HD, int USTEP>
-__device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, int npos, float scale, int lane,
-                                          int u0) {
+// The wave takes units u0, u0 + USTEP, ... of the page (USTEP = 1: all of them); with
+// NP > 1, of each of NP pages at once (one running-max update for all of them).
+template <int HD, int USTEP, int NP = 1>
+__device__ __forceinline__ void head_page(HeadState<HD>& st, const char* const (&pages)[NP], const int (&nposv)[NP],
+                                          float scale, int lane, int u0) {
   constexpr int LPP = HD / 8;          // lanes per position
   constexpr int PPU = 64 / LPP;        // positions per 1 KiB unit
   constexpr int MAXU = 8 / USTEP;      // units per key block (16 KiB page) for this wave
-  const int kbytes = npos * HD * 2;
+  constexpr int NU = NP * MAXU;
   const int jl = lane / LPP;
-  uint4 kw[MAXU], vw[MAXU];
+  uint4 kw[NU], vw[NU];
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) kw[u] = *(const uint4*)(page + (u0 + u * USTEP) * 1024 + lane * 16);
+  for (int pi = 0; pi < NP; ++pi)
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) vw[u] = *(const uint4*)(page + kbytes + (u0 + u * USTEP) * 1024 + lane * 16);
-  float s[MAXU];
+    for (int u = 0; u < MAXU; ++u) kw[pi * MAXU + u] = *(const uint4*)(pages[pi] + (u0 + u * USTEP) * 1024 + lane * 16);
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) {
-    float part = dot8(kw[u], st.q, 0.f);
-    part = LPP == 8 ? sum8(part) : sum16(part);
-    s[u] = (u0 + u * USTEP) * PPU + jl < npos ? part * scale : -INFINITY;
-  }
+  for (int pi = 0; pi < NP; ++pi)
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u)
+      vw[pi * MAXU + u] = *(const uint4*)(pages[pi] + nposv[pi] * HD * 2 + (u0 + u * USTEP) * 1024 + lane * 16);
+  float s[NU];
+#pragma unroll
+  for (int pi = 0; pi < NP; ++pi)
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+      float part = dot8(kw[pi * MAXU + u], st.q, 0.f);
+      part = LPP == 8 ? sum8(part) : sum16(part);
+      s[pi * MAXU + u] = (u0 + u * USTEP) * PPU + jl < nposv[pi] ? part * scale : -INFINITY;
+    }
   float pm = s[0];
 #pragma unroll
-  for (int u = 1; u < MAXU; ++u) pm = fmaxf(pm, s[u]);
+  for (int u = 1; u < NU; ++u) pm = fmaxf(pm, s[u]);
   pm = wave_max(pm);
   const float mn = fmaxf(st.m, pm);
   const float alpha = st.m == -INFINITY ? 0.f : __expf(st.m - mn);
@@ -978,7 +986,7 @@ __device__ __forceinline__ void head_page(HeadState<HD>& st, const char* page, i
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.o[e] *= alpha;
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const float pr = __expf(s[u] - mref);   // exactly 0 for positions past npos
     st.l += pr;
     st.o[0] = fmaf(pr, bf_lo(vw[u].x), st.o[0]);
@@ -1029,20 +1037,44 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
       prev_k = -1;
     }
   };
-  for (int pg = qh ? 0 : t; pg < d.np; pg += qh ? 1 : NSUB) {
+  for (int pg = qh ? 0 : t; pg < d.np;) {
     const int k = base + pg;
     const char* page = page_wait<S>(p, sh, ring_base, k, waited);
     if (!page) return false;
     const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
+    if (qh && pg + 1 < d.np) {
+      // q-head mode: two pages at a time (one running-max update for both)
+      const char* page2 = page_wait<S>(p, sh, ring_base, k + 1, waited);
+      if (!page2) return false;
+      const char* const pp[2] = {page, page2};
+      const int nn[2] = {npos, min(S::PPP, d.ce - (d.j0 + (pg + 1) * S::PPP))};
+      head_page<HD, MK_NC, 2>(st, pp, nn, p.attn_scale, lane, w);
+      release_prev();
+      int old = 0, old2 = 0;
+      if (lane == 0) {
+        old = atomicAdd(&sh.acnt[k % NSLOT], 1);
+        old2 = atomicAdd(&sh.acnt[(k + 1) % NSLOT], 1);
+      }
+      prev_k = k;
+      prev_old = old;
+      release_prev();
+      prev_k = k + 1;
+      prev_old = old2;
+      pg += 2;
+      continue;
+    }
+    const char* const pp[1] = {page};
+    const int nn[1] = {npos};
     if (qh)
-      head_page<HD, MK_NC>(st, page, npos, p.attn_scale, lane, w);
+      head_page<HD, MK_NC>(st, pp, nn, p.attn_scale, lane, w);
     else
-      head_page<HD, 1>(st, page, npos, p.attn_scale, lane, 0);
+      head_page<HD, 1>(st, pp, nn, p.attn_scale, lane, 0);
     release_prev();
     int old = 0;
     if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
     prev_k = k;
     prev_old = old;
+    pg += qh ? 1 : NSUB;
   }
   release_prev();
   // Sum over the lanes holding other positions (same dims): xor LPP .. 32.
