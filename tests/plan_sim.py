@@ -49,7 +49,6 @@ def simulate(shape, plan, pos):
     merged = set()                     # (cu, instr index) items published
     nch = max([int(r[7]) for r in rec if int(r[0]) == DOWN] or [1])
     csz = F // nch
-    fpp = max(1, plan["page_bytes"] // (4 * d))   # gate/up features per page
 
     def group_of_qkv_row(r):
         if r < nq:
@@ -98,8 +97,9 @@ def simulate(shape, plan, pos):
                     if x_rows[2 * layer + 1] < d:
                         break
                     rs = int(rec[ptr[c]][10])
+                    fb = 1 << a                    # features per block (log2 in field a)
                     for q in range(n):
-                        f = r0 + (q // fpp) * rs + q % fpp
+                        f = r0 + (q // fb) * rs + q % fb
                         a_rows[(layer, f // csz)] += 1
                 elif op == DOWN:
                     if a_rows[(layer, a)] < kn:

@@ -74,9 +74,13 @@ def test_plan_partitions_every_matrix_exactly(name, n_cus):
             op, layer, r0, n, k0, kn, a, b = r[:8]
             cover.setdefault((op, layer, a if op == OPS["DOWN"] else 0), []).append((r0, n, k0, kn, a, b))
             if op == OPS["GATEUP"]:
-                # features come a page group at a time: q -> r0 + (q // fpp) * rs + q % fpp
+                # features come a block of 2^a at a time: q -> r0 + (q // fb) * rs + q % fb,
+                # a block being a page's features or (where every CU gets whole blocks per
+                # down chunk) eight, one 64-byte line of link words
                 fpp = max(1, P["page_bytes"] // (4 * s.hidden))
-                feats.setdefault(layer, []).extend(r0 + (q // fpp) * int(r[10]) + q % fpp for q in range(n))
+                fb = 1 << int(a)
+                assert fb == fpp or (fb == 8 and fpp < 8), (fb, fpp)
+                feats.setdefault(layer, []).extend(r0 + (q // fb) * int(r[10]) + q % fb for q in range(n))
             if op == OPS["QKV"]:
                 assert (k0, kn) == (0, s.hidden)
             if op == OPS["O"]:

@@ -451,12 +451,12 @@ __device__ __forceinline__ Dec decode(const MkParams& p, const MkInstr& in, cons
   return d;
 }
 
-// Feature of the GATEUP instruction's q-th feature: the features come a page (FPP
-// features) at a time, one page group per rs features of the intermediate.
+// Feature of the GATEUP instruction's q-th feature: the features come in blocks of 2^a
+// (a page's features, or eight: one 64-byte line of link words), one block per rs
+// features of the intermediate.
 template <class S>
 __device__ __forceinline__ int gu_feature(const Dec& d, int q) {
-  constexpr int FPP = MK_PAGE_BYTES / (4 * S::D);
-  return d.r0 + (q / FPP) * d.rs + q % FPP;
+  return d.r0 + (q >> d.a) * d.rs + (q & ((1 << d.a) - 1));   // blocks of 2^a features
 }
 
 // Address of row pr of the instruction, for one opcode.  GATEUP rows interleave gate(f),

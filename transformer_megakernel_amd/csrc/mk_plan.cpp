@@ -116,18 +116,25 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
     // the odd XCDs streamed their blocks a few per cent slower (they finished the LM head
     // 2-4 us after the even ones); with this split the slowest CU finishes ~2 us earlier.
     split_xcd(c.vocab, n_cus, cu, n_cus % 8 == 0 ? 0.04 : 0.0, &v0, &vn);
-    // Gate/up features are dealt one page (fpp features) at a time, round-robin over the
-    // CUs: feature page pg goes to CU pg % n_cus.  A CU's first pages then feed the first
-    // down chunk, its next pages the second, and so on, so chunk k is complete once every
-    // CU has passed its k-th quarter, long before the slowest CU finishes, and the down
-    // chunks' staging overlaps the gate/up streaming.  Feature q of the instruction is
-    // r0 + (q / fpp) * rs + q % fpp.
+    // Gate/up features are dealt in blocks of fb features, round-robin over the CUs:
+    // block b goes to CU b % n_cus.  A CU's first pages then feed the first down chunk,
+    // its next pages the second, and so on, so chunk k is complete once every CU has
+    // passed its k-th quarter, long before the slowest CU finishes, and the down chunks'
+    // staging overlaps the gate/up streaming.  A block is one page's features (fpp), or
+    // eight features (a 64-byte line of link words) where that still gives every CU a whole
+    // number of blocks per down chunk: each line of SiLU(g)*u words is then written by one
+    // CU only.  Feature q of the instruction is r0 + (q / fb) * rs + q % fb (fb a power of
+    // two, log2 in the instruction's field a).
     const int fpp = std::max(1, MK_PAGE_BYTES / (4 * d));
-    const int fpages = (c.ffn + fpp - 1) / fpp;
-    f0 = cu * fpp;
+    int fb = fpp;
+    if (fpp < 8 && (c.ffn / nch) % (n_cus * 8) == 0 && c.ffn % nch == 0) fb = 8;
+    const int fblocks = (c.ffn + fb - 1) / fb;
+    f0 = cu * fb;
     fn = 0;
-    for (int pg = cu; pg < fpages; pg += n_cus) fn += std::min(fpp, c.ffn - pg * fpp);
-    const int fstride = n_cus * fpp;
+    for (int b = cu; b < fblocks; b += n_cus) fn += std::min(fb, c.ffn - b * fb);
+    const int fstride = n_cus * fb;
+    int fb_log2 = 0;
+    while ((1 << fb_log2) < fb) ++fb_log2;
     for (int l = 0; l < c.n_layers; ++l) {
       MkInstr q = mk(MK_OP_QKV, l);
       q.r0 = q0; q.n = qn; q.k0 = 0; q.kn = d;
@@ -147,7 +154,7 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
         p.rec.push_back(o);
       }
       MkInstr gu = mk(MK_OP_GATEUP, l);
-      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d; gu.rs = fstride;
+      gu.r0 = f0; gu.n = fn; gu.k0 = 0; gu.kn = d; gu.rs = fstride; gu.a = fb_log2;
       p.rec.push_back(gu);
       if (on > 0) {
         for (int k = 0; k < nch; ++k) {
