@@ -1077,6 +1077,40 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
     pg += qh ? 1 : NSUB;
   }
   release_prev();
+  if (qh || NSUB > 1) {
+    // Partial (m, l, o) for the leader (q-head mode: one slot per wave).  The sum over the
+    // lanes holding other positions halves the values at each step: the lanes at distance
+    // 32, then 16 (then 8, hd 64), trade half of their dims and add, so that each lane ends
+    // with 8 / positions-per-unit dims (lane swaps, one DPP move; instead of 9 sums per step).
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = st.o[e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = swap_sum32(v[e], v[e + 4]);   // dim e + 4 * b5
+#pragma unroll
+    for (int e = 0; e < 2; ++e) v[e] = swap_sum16(v[e], v[e + 2]);   // dim e + 2 * b4 + 4 * b5
+    float L = st.l;
+    if constexpr (LPP == 8) {
+      const uint32_t m8 = (lane & 8) ? 0xffffffffu : 0u;
+      const uint32_t a = __float_as_uint(v[0]), b = __float_as_uint(v[1]);
+      v[0] = __uint_as_float((b & m8) | (a & ~m8)) + xor_lane<8>(__uint_as_float((a & m8) | (b & ~m8)), lane);
+      L += xor_lane<8>(L, lane);
+    }
+    L = swap_sum16(L, L);
+    L = swap_sum32(L, L);
+    float* part = qh ? &sh.part[0][0][0] + w * (HD + 2) : sh.part[t][h];
+    if constexpr (LPP == 8) {
+      part[2 + c * 8 + (lane >> 3)] = v[0];   // dim 8c + b3 + 2 b4 + 4 b5
+    } else {
+      part[2 + c * 8 + 2 * (lane >> 4)] = v[0];
+      part[2 + c * 8 + 2 * (lane >> 4) + 1] = v[1];
+    }
+    if (lane == 0) {
+      part[0] = st.m;
+      part[1] = L;
+    }
+    return true;
+  }
   // Sum over the lanes holding other positions (same dims): xor LPP .. 32.
 #pragma unroll
   for (int off = LPP; off < 64; off <<= 1) {
@@ -1088,19 +1122,6 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
     st.l += tt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.o[e] += tt[e];
-  }
-  if (qh || NSUB > 1) {
-    // partial (m, l, o) for the leader; q-head mode: one slot per wave
-    float* part = qh ? &sh.part[0][0][0] + w * (HD + 2) : sh.part[t][h];
-    if (lane < LPP) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part[2 + lane * 8 + e] = st.o[e];
-    }
-    if (lane == 0) {
-      part[0] = st.m;
-      part[1] = st.l;
-    }
-    return true;
   }
   // One head per wave: fold in the current position (its key is not in the cache yet).
   const int s = d.b;
