@@ -1077,90 +1077,66 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
     pg += qh ? 1 : NSUB;
   }
   release_prev();
+  // Sum over the lanes holding other positions (same dims), halving the values at each
+  // step: the lanes at distance 32, then 16 (then 8, hd 64) trade half of their dims and
+  // add (lane swaps and one DPP move, instead of all nine values at every step).  Lane l
+  // then holds the NE = 8 / (positions per unit) dims dim(l) + j, j < NE.
+  constexpr int NE = LPP == 8 ? 1 : 2;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = st.o[e];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = swap_sum32(v[e], v[e + 4]);   // dim e + 4 * b5
+#pragma unroll
+  for (int e = 0; e < 2; ++e) v[e] = swap_sum16(v[e], v[e + 2]);   // dim e + 2 * b4 + 4 * b5
+  float L = st.l;
+  if constexpr (LPP == 8) {
+    const uint32_t m8 = (lane & 8) ? 0xffffffffu : 0u;
+    const uint32_t a = __float_as_uint(v[0]), b = __float_as_uint(v[1]);
+    v[0] = __uint_as_float((b & m8) | (a & ~m8)) + xor_lane<8>(__uint_as_float((a & m8) | (b & ~m8)), lane);
+    L += xor_lane<8>(L, lane);
+  }
+  L = swap_sum16(L, L);
+  L = swap_sum32(L, L);
+  const int dim = LPP == 8 ? c * 8 + (lane >> 3) : c * 8 + 2 * (lane >> 4);
   if (qh || NSUB > 1) {
-    // Partial (m, l, o) for the leader (q-head mode: one slot per wave).  The sum over the
-    // lanes holding other positions halves the values at each step: the lanes at distance
-    // 32, then 16 (then 8, hd 64), trade half of their dims and add, so that each lane ends
-    // with 8 / positions-per-unit dims (lane swaps, one DPP move; instead of 9 sums per step).
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = st.o[e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = swap_sum32(v[e], v[e + 4]);   // dim e + 4 * b5
-#pragma unroll
-    for (int e = 0; e < 2; ++e) v[e] = swap_sum16(v[e], v[e + 2]);   // dim e + 2 * b4 + 4 * b5
-    float L = st.l;
-    if constexpr (LPP == 8) {
-      const uint32_t m8 = (lane & 8) ? 0xffffffffu : 0u;
-      const uint32_t a = __float_as_uint(v[0]), b = __float_as_uint(v[1]);
-      v[0] = __uint_as_float((b & m8) | (a & ~m8)) + xor_lane<8>(__uint_as_float((a & m8) | (b & ~m8)), lane);
-      L += xor_lane<8>(L, lane);
-    }
-    L = swap_sum16(L, L);
-    L = swap_sum32(L, L);
+    // partial (m, l, o) for the leader; q-head mode: one slot per wave
     float* part = qh ? &sh.part[0][0][0] + w * (HD + 2) : sh.part[t][h];
-    if constexpr (LPP == 8) {
-      part[2 + c * 8 + (lane >> 3)] = v[0];   // dim 8c + b3 + 2 b4 + 4 b5
-    } else {
-      part[2 + c * 8 + 2 * (lane >> 4)] = v[0];
-      part[2 + c * 8 + 2 * (lane >> 4) + 1] = v[1];
-    }
+#pragma unroll
+    for (int j = 0; j < NE; ++j) part[2 + dim + j] = v[j];
     if (lane == 0) {
       part[0] = st.m;
       part[1] = L;
     }
     return true;
   }
-  // Sum over the lanes holding other positions (same dims): xor LPP .. 32.
-#pragma unroll
-  for (int off = LPP; off < 64; off <<= 1) {
-    float tt[9];
-    tt[8] = off == 8 ? xor_lane<8>(st.l, lane) : off == 16 ? xor_lane<16>(st.l, lane) : xor_lane<32>(st.l, lane);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      tt[e] = off == 8 ? xor_lane<8>(st.o[e], lane) : off == 16 ? xor_lane<16>(st.o[e], lane) : xor_lane<32>(st.o[e], lane);
-    st.l += tt[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.o[e] += tt[e];
-  }
   // One head per wave: fold in the current position (its key is not in the cache yet).
   const int s = d.b;
   const bool has_pos = s == g.s_eff - 1;
-  float M = st.m, L = st.l, o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = st.o[e];
+  float M = st.m;
   if (has_pos) {
-    float kc[8], vc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kc[e] = act[HPG * HD + c * 8 + e];
-      vc[e] = act[(HPG + 1) * HD + c * 8 + e];
-    }
     float sc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc = fmaf(st.q[e], kc[e], sc);
+    for (int e = 0; e < 8; ++e) sc = fmaf(st.q[e], act[HPG * HD + c * 8 + e], sc);
     sc = (LPP == 8 ? sum8(sc) : sum16(sc)) * p.attn_scale;
     const float Mn = fmaxf(M, sc);
     const float a = M == -INFINITY ? 0.f : __expf(M - Mn);
     const float b = __expf(sc - Mn);
     L = L * a + b;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = fmaf(o[e], a, b * vc[e]);
+    for (int j = 0; j < NE; ++j) v[j] = fmaf(v[j], a, b * act[(HPG + 1) * HD + dim + j]);
     M = Mn;
   }
+  // every lane stores its dims: one full line per store instruction
   const int l = d.layer, gi = d.a;
   if (g.s_eff == 1) {
-    u64* dst = p.ll_o + (size_t)l * S::NQ + (gi * HPG + h) * HD + lane * 8;
-    if (lane < LPP) {
+    u64* dst = p.ll_o + (size_t)l * S::NQ + (gi * HPG + h) * HD + dim;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ll_store(dst + e, o[e] / L, epoch);
-    }
+    for (int j = 0; j < NE; ++j) ll_store(dst + j, v[j] / L, epoch);
   } else {
     u64* dst = p.ll_part + part_index<S>(p, l, gi, h, s);
-    if (lane < LPP) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ll_store(dst + 2 + lane * 8 + e, o[e], epoch);
-    }
+    for (int j = 0; j < NE; ++j) ll_store(dst + 2 + dim + j, v[j], epoch);
     if (lane == 0) {
       ll_store(dst, M, epoch);
       ll_store(dst + 1, L, epoch);
