@@ -658,8 +658,12 @@ __device__ __forceinline__ int first_of(int who, int base, int period) {
 
 // Loader wave l.  It publishes its pages in order, each once vmcnt shows it complete.
 // Two pacing modes, chosen per page:
-//  - demand: the page's instruction is already staged, so compute waves are (or soon will
-//    be) waiting for it; keep up to DEPTH of the wave's pages in flight for bandwidth.
+//  - demand: the page's instruction is staged, or about to be, so compute waves are (or
+//    soon will be) waiting for it; keep up to DEPTH of the wave's pages in flight for
+//    bandwidth.  A down chunk's pages count as such from the layer's gate/up staging on
+//    (its chunks follow back to back; 538.4 vs 543.1 us per step, against from the
+//    chunk's own staging), those of QKV, attention and O from the previous instruction's
+//    staging (a further 0.9 us).
 //  - prefetch: the page is for a later instruction; keep a single page in flight for the
 //    whole CU (the two loaders take turns).  A CU's vector-memory requests are served in
 //    order, so every poll of a dependency and every result store queues behind the bytes
@@ -706,7 +710,11 @@ __device__ __forceinline__ void loader_wave(const MkParams& p, MkShared<S>& sh, 
         wait_vmcnt((pend - 1) * 16);
         publish_oldest();
       }
-      const bool demand = lds_load(&sh.act_seq) >= i + 1;
+      // Demand from: the layer's gate/up staged (down chunks), the previous instruction
+      // staged (QKV, attention, O), the instruction itself staged (gate/up, LM head).
+      const int from = d.op == MK_OP_DOWN ? i - d.a
+                       : (d.op == MK_OP_QKV || d.op == MK_OP_ATTN || d.op == MK_OP_O) ? i : i + 1;
+      const bool demand = lds_load(&sh.act_seq) >= from;
       if (!demand && k > 0) {
         // Prefetch: own pages first (the other loader may be waiting for one), then the other
         // loader's page k - 1 must have landed (one page in flight per CU; two per CU measured
