@@ -179,3 +179,16 @@ def test_plan_simulator_reports_planted_deadlocks(pos):
     circular = _move_before(P, 11, lambda r: r[0] == OPS["DOWN"] and r[1] == 3 and r[6] == 0,
                             lambda r: r[0] == OPS["GATEUP"] and r[1] == 3)
     assert not simulate(s, circular, pos)[0]
+
+
+@pytest.mark.parametrize("pos,splits", [(0, 1), (1, 1), (128, 1), (256, 1), (257, 2), (300, 2),
+                                        (1024, 4), (1279, 5), (8191, 32), (8192, 32)])
+def test_attention_splits_cover_the_cached_keys(pos, splits):
+    """Keys 0..pos-1 are in the cache and split into runs of at least 256 (a whole number
+    of pages), at most one per CU of a KV head's share; the current key joins the last
+    split, so no split ever holds it alone."""
+    from tests.plan_sim import split_geometry
+    s = ModelShape.named("llama1b")
+    P = mk.Megakernel.plan_only(s, 8193, 256).plan()
+    assert P["s_max"] == 32
+    assert split_geometry(s, P, pos) == splits

@@ -337,7 +337,7 @@ __device__ __forceinline__ void trace_max(const MkParams& p, MkShared<S>& sh, in
 
 // ------------------------------------------------------------------ step geometry
 struct StepGeo {
-  int pos, s_eff, chunk;   // attention split of keys 0..pos
+  int pos, s_eff, chunk;   // attention split of the cached keys 0..pos-1
   int qh;                  // one split: item (g, b < HPG) computes query head g * HPG + b
 };
 
@@ -353,7 +353,11 @@ template <class S>
 __device__ __forceinline__ StepGeo step_geo(const MkParams& p, int pos) {
   StepGeo g;
   g.pos = pos;
-  const int nk = pos + 1;
+  // The splits cover the cached keys 0..pos-1; the current key joins the last split.
+  // (Splitting keys 0..pos instead left a split holding the current key alone whenever
+  // pos was a multiple of the split size, and at pos 8192 forced 320-key splits, 26 of
+  // them instead of 32 of 256: 687.6 vs 680.0 us per step.)
+  const int nk = pos > 1 ? pos : 1;
   int chunk = (nk + p.s_max - 1) / p.s_max;
   if (chunk < p.min_chunk) chunk = p.min_chunk;
   chunk = (chunk + S::PPP - 1) / S::PPP * S::PPP;
