@@ -82,11 +82,28 @@ struct Traced : B {
   static constexpr bool TRACE = true;
 };
 
+// Attention items with several splits.  head_dim 64: on the matrix units, every compute
+// wave taking a quarter of each page's keys for all of the group's query heads (KS = 4
+// key subsets); otherwise one query head per wave (KS = MK_NC / HPG subsets per head).
+// The subsets' partials (m, l, o) per head go to the activation slot, after q|k|v, where
+// there is room, else to their own LDS array.
+template <class S>
+struct AttnGeo {
+  static constexpr bool MMA = S::HD == 64 && S::HPG <= 4 && S::PPP == 64;
+  static constexpr int KS = MMA ? MK_NC : MK_NC / S::HPG;
+  static constexpr int PART = KS * S::HPG * (S::HD + 2);     // floats of partials
+  static constexpr int OFF = (S::GRP + 63) / 64 * 64;        // their offset in the slot
+  static constexpr bool IN_ACT = OFF + PART <= S::ACT;
+  static constexpr int OWN = IN_ACT ? 0 : PART;              // floats of the LDS array
+  // q-head mode keeps one (m, l, o) per compute wave in the array
+  static constexpr int LDS = cmax(MK_NC * (S::HD + 2), OWN);
+};
+
 // LDS of one work-group (the page ring is a separate array).
 template <class S>
 struct __align__(16) MkShared {
   float act[MK_NACT][S::ACT];               // staged activation vectors (ring)
-  float part[MK_NC / S::HPG][S::HPG][S::HD + 2];   // attention partials (m, l, o) per key subset and head
+  float part[AttnGeo<S>::LDS];              // attention partials (m, l, o): q-head mode, key subsets
   static_assert(MK_NC % S::HPG == 0, "query heads per KV head must divide the compute waves");
   int acnt[MK_MAX_SLOTS];                   // readers done with the attention page in a slot
   float xres[2][MK_MAX_RES_ROWS];           // x rows for the residual of O (0) and DOWN (1)
@@ -173,6 +190,11 @@ __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16 bits, round to nearest, ties to even (quiet NaN kept).
+// bf16 bits of a finite float, rounded to nearest even (no NaN case: no branches)
+__device__ __forceinline__ uint16_t f2bf_finite(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
@@ -942,7 +964,10 @@ __device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, in
 }
 
 // ------------------------------------------------------------------ attention
-// Compute wave w handles query head h = w % HPG of the item's KV group over the key
+// Short contexts (one split, q-head mode): item (g, b) is query head b of KV group g and
+// the four compute waves split the keys.  Several splits: head_dim 64 goes to the matrix
+// units (attn_run_mma: each wave a quarter of every page's keys, all heads).  Otherwise
+// compute wave w handles query head h = w % HPG of the item's KV group over the key
 // subset t = w / HPG (pages t, t + NSUB, ... of the split; NSUB = MK_NC / HPG): with four
 // query heads per KV head every wave sees every page and owns its head outright, so no
 // cross-wave merge is needed.  Each page is read by HPG waves and freed by the last.
@@ -1015,6 +1040,148 @@ __device__ __forceinline__ void head_page(HeadState<HD>& st, const char* const (
   }
 }
 
+// Where the key subsets' partials of an attention item live (the item's activation slot
+// or the LDS array): [subset][head][m, l, o[HD]].
+template <class S>
+__device__ __forceinline__ float* part_base(MkShared<S>& sh, const float* act) {
+  if constexpr (AttnGeo<S>::IN_ACT) return const_cast<float*>(act) + AttnGeo<S>::OFF;
+  else return sh.part;
+}
+
+// Attention over the item's cached keys on the matrix units (head_dim 64, several splits):
+// wave w takes keys 16w..16w+15 of every page for all of the group's query heads, so
+// each K/V element is unpacked once per CU instead of once per head.  Per page:
+//   S = K q   (16 keys x 16 head columns, two 16x16x32 bf16 products per 32 dims; q is
+//              split into bf16 hi + lo parts, so the scores keep ~16 significant bits),
+//   an online softmax per head over the wave's keys (its running max is shared by the
+//   four lanes of a column),
+//   O += P V  (16 heads x 64 dims as four 16x16x16 bf16 products; P split hi + lo).
+// Operand layouts (lane l, c = l % 16, g = l / 16): A[row c][k 8g..] (16x16x32) or
+// [row c][k 4g..] (16x16x16); B[k ...][column c]; C/D[rows 4g..4g+3][column c].  The
+// scores' C layout (key 4g + i, head c) is exactly the A layout P needs (head c, key
+// 4g + j), so P goes from softmax to the product without moving.  Columns c >= HPG are
+// padding (q = 0, P = 0).  The partials go to the leader, which adds the current key.
+template <class S>
+__device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
+                                             const float* act, int base, int w, int lane, u64& waited) {
+  constexpr int HD = S::HD, HPG = S::HPG, NSLOT = Ring<S>::NSLOT;
+  static_assert(AttnGeo<S>::MMA && HD == 64 && S::PPP == 64 && MK_NC == 4, "matrix-unit attention shape");
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int c = lane & 15, g = lane >> 4;
+  // q as B: column c = head, k = dims 8g + 32kk + e (padding columns read head 0's q and
+  // take zeros)
+  bf16x8 qh[2], ql[2];
+  const float* qc = act + (c < HPG ? c : 0) * HD + 8 * g;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const float4 x0 = *(const float4*)(qc + 32 * kk), x1 = *(const float4*)(qc + 32 * kk + 4);
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = c < HPG ? xs[e] : 0.f;
+      const uint32_t xb = __float_as_uint(x);
+      qh[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)(xb >> 16));
+      ql[kk][e] = __builtin_bit_cast(__bf16, f2bf_finite(x - __uint_as_float(xb & 0xffff0000u)));
+    }
+  }
+  f32x4 o[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;   // running max of head c; this lane's part of its denominator
+  int prev_k = -1, prev_old = 0;
+  auto release_prev = [&]() {
+    if (prev_k >= 0) {
+      const int old = __shfl(prev_old, 0);
+      if (old == MK_NC - 1 && lane == 0) {
+        sh.acnt[prev_k % NSLOT] = 0;
+        lds_store(&sh.freed[prev_k % NSLOT], prev_k + 1);
+      }
+      prev_k = -1;
+    }
+  };
+  const int kr = 16 * w + c;            // the key row this lane loads for A = K
+  const int vr = 16 * w + 4 * g;        // first of the four key rows it loads for B = V
+  for (int pg = 0; pg < d.np; ++pg) {
+    const int k = base + pg;
+    const char* page = page_wait<S>(p, sh, ring_base, k, waited);
+    if (!page) return false;
+    const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
+    // keys [npos][HD], then values [npos][HD]; rows past npos hold copies of cached rows
+    const bf16x8 k0 = *(const bf16x8*)(page + kr * (HD * 2) + g * 16);
+    const bf16x8 k1 = *(const bf16x8*)(page + kr * (HD * 2) + g * 16 + 64);
+    const char* vb = page + npos * (HD * 2) + vr * (HD * 2) + c * 2;
+    i16x4 vv[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vv[nt][j] = *(const short*)(vb + j * (HD * 2) + nt * 32);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qh[0], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, ql[0], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qh[1], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, ql[1], sc, 0, 0, 0);
+    float sv[4], pm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = vr + i < npos ? sc[i] * p.attn_scale : -INFINITY;
+      pm = fmaxf(pm, sv[i]);
+    }
+    pm = fmaxf(pm, xor16(pm, lane));
+    pm = fmaxf(pm, xor32(pm, lane));
+    const float mn = fmaxf(m, pm);
+    const float alpha = m == -INFINITY ? 0.f : __expf(m - mn);
+    const float mref = mn == -INFINITY ? 0.f : mn;   // -inf only while no key has been seen
+    m = mn;
+    i16x4 ph, pl;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pr = c < HPG ? __expf(sv[j] - mref) : 0.f;   // 0 for keys past npos
+      ps += pr;
+      const uint32_t pb = __float_as_uint(pr);
+      ph[j] = (short)(pb >> 16);
+      pl[j] = (short)f2bf_finite(pr - __uint_as_float(pb & 0xffff0000u));
+    }
+    lsum = fmaf(lsum, alpha, ps);
+    // O's rows 4g + i are heads; heads 0..3 sit in lanes 0..15 (g = 0), and head h's
+    // factor is alpha of column h
+    float ah[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ah[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nt][i] *= ah[i];
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vv[nt], o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vv[nt], o[nt], 0, 0, 0);
+    }
+    // the page's last reader frees it (its count examined one page later)
+    release_prev();
+    int old = 0;
+    if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
+    prev_k = k;
+    prev_old = old;
+  }
+  release_prev();
+  // head c's denominator: the four lanes of column c
+  float L = lsum + xor16(lsum, lane);
+  L += xor32(L, lane);
+  float* part = part_base<S>(sh, act) + w * HPG * (HD + 2);
+  if (g == 0 && c < HPG) {
+    part[c * (HD + 2)] = m;
+    part[c * (HD + 2) + 1] = L;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < HPG; ++i) part[i * (HD + 2) + 2 + 16 * nt + c] = o[nt][i];
+  }
+  return true;
+}
+
 // The item's cached keys for one head, then (one head per wave) the current position's
 // key and value, and the result: o / l into the attention output (one split) or the
 // split's (m, l, o) words; with several waves per head the partial goes to LDS and the
@@ -1024,6 +1191,9 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
                                          const StepGeo& g, const float* act, int base, int w, int lane,
                                          uint32_t epoch, u64& waited) {
   constexpr int HD = S::HD, HPG = S::HPG, LPP = HD / 8, NSUB = MK_NC / HPG, NSLOT = Ring<S>::NSLOT;
+  if constexpr (AttnGeo<S>::MMA) {
+    if (!g.qh) return attn_run_mma<S>(p, sh, ring_base, d, act, base, w, lane, waited);
+  }
   // q-head mode: head d.b of the group; every wave reads every page and takes units
   // w, w + MK_NC of it.  Otherwise one head per wave (w % HPG) over pages t, t + NSUB, ...
   const bool qh = g.qh;
@@ -1116,7 +1286,7 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
   const int dim = LPP == 8 ? c * 8 + (lane >> 3) : c * 8 + 2 * (lane >> 4);
   if (qh || NSUB > 1) {
     // partial (m, l, o) for the leader; q-head mode: one slot per wave
-    float* part = qh ? &sh.part[0][0][0] + w * (HD + 2) : sh.part[t][h];
+    float* part = qh ? sh.part + w * (HD + 2) : part_base<S>(sh, act) + (t * HPG + h) * (HD + 2);
 #pragma unroll
     for (int j = 0; j < NE; ++j) part[2 + dim + j] = v[j];
     if (lane == 0) {
@@ -1462,7 +1632,7 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
 template <class S>
 __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh, const MkInstr& in,
                                               const StepGeo& g, int i, uint32_t epoch, int lane) {
-  constexpr int HD = S::HD, HPG = S::HPG, E = HD / 64, STRIDE = HD + 2, NSUB = MK_NC / HPG;
+  constexpr int HD = S::HD, HPG = S::HPG, E = HD / 64, STRIDE = HD + 2, NSUB = AttnGeo<S>::KS;
   const int l = in.layer, gi = in.a, s = in.b;
   const float* act = sh.act[i % MK_NACT];
   if (g.qh) {
@@ -1470,7 +1640,7 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
     // The current key's score is formed while the compute waves still work; the leader
     // then waits for them (the caller does not).
     if (s >= HPG) return wait_all_done(p, sh, i + 1, true);
-    const float* pb = &sh.part[0][0][0];
+    const float* pb = sh.part;
     float mw[MK_NC], lw[MK_NC], ow[MK_NC][E], kn[E], vn[E];
     float sp = 0.f;
 #pragma unroll
@@ -1510,15 +1680,17 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
   }
   if (NSUB > 1 && s < g.s_eff) {
     const bool has_pos = s == g.s_eff - 1;
+    const float* pb = part_base<S>(sh, act);
     float mw[NSUB][HPG], lw[NSUB][HPG], ow[NSUB][HPG][E], qv[HPG][E], kn[E], vn[E];
 #pragma unroll
     for (int w = 0; w < NSUB; ++w)
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
-        mw[w][h] = sh.part[w][h][0];
-        lw[w][h] = sh.part[w][h][1];
+        const float* q = pb + (w * HPG + h) * STRIDE;
+        mw[w][h] = q[0];
+        lw[w][h] = q[1];
 #pragma unroll
-        for (int c = 0; c < E; ++c) ow[w][h][c] = sh.part[w][h][2 + c * 64 + lane];
+        for (int c = 0; c < E; ++c) ow[w][h][c] = q[2 + c * 64 + lane];
       }
 #pragma unroll
     for (int c = 0; c < E; ++c) {
@@ -1701,7 +1873,7 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
       // Partials in LDS only when several waves share a head; a merge polls global words.
       // (In q-head mode attn_finalize waits itself, after the current key's score.)
       if (!g.qh) {
-        if (MK_NC > S::HPG && !wait_all_done(p, sh, i + 1, true)) return;
+        if (AttnGeo<S>::KS > 1 && !wait_all_done(p, sh, i + 1, true)) return;
         trace_mark<S>(p, sh, i, 8, lane);
       }
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
