@@ -880,7 +880,7 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
       int old = 0;
       if (lane == 0) old = atomicAdd(&sh.acnt[k % NSLOT], 1);
       const float v = reduce_rows<2, 64>(acc, lane);
-      old = __shfl(old, 0);
+      old = __builtin_amdgcn_readlane(old, 0);
       if (old == 1 && lane == 0) {
         sh.acnt[k % NSLOT] = 0;
         lds_store(&sh.freed[k % NSLOT], k + 1);
@@ -1093,7 +1093,7 @@ __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh,
   int prev_k = -1, prev_old = 0;
   auto release_prev = [&]() {
     if (prev_k >= 0) {
-      const int old = __shfl(prev_old, 0);
+      const int old = __builtin_amdgcn_readlane(prev_old, 0);   // lane 0's count, no LDS trip
       if (old == MK_NC - 1 && lane == 0) {
         sh.acnt[prev_k % NSLOT] = 0;
         lds_store(&sh.freed[prev_k % NSLOT], prev_k + 1);
@@ -1214,7 +1214,7 @@ __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, con
   int prev_k = -1, prev_old = 0;
   auto release_prev = [&]() {
     if (prev_k >= 0) {
-      const int old = __shfl(prev_old, 0);
+      const int old = __builtin_amdgcn_readlane(prev_old, 0);   // lane 0's count, no LDS trip
       if (old == readers - 1 && lane == 0) {
         sh.acnt[prev_k % NSLOT] = 0;
         lds_store(&sh.freed[prev_k % NSLOT], prev_k + 1);
