@@ -1709,6 +1709,7 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
     }
 #pragma unroll
     for (int h = 0; h < HPG; ++h) sp[h] = has_pos ? wave_sum(sp[h]) * p.attn_scale : -INFINITY;
+    float Mh[HPG], Lh[HPG];
 #pragma unroll
     for (int h = 0; h < HPG; ++h) {
       float M = sp[h];
@@ -1733,10 +1734,17 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
         else
           ll_store(p.ll_part + part_index<S>(p, l, gi, h, s) + 2 + e, o, epoch);
       }
-      if (g.s_eff > 1 && lane == 0) {
-        ll_store(p.ll_part + part_index<S>(p, l, gi, h, s), M, epoch);
-        ll_store(p.ll_part + part_index<S>(p, l, gi, h, s) + 1, L, epoch);
-      }
+      Mh[h] = M;
+      Lh[h] = L;
+    }
+    if (g.s_eff > 1) {
+      // every head's (m, l) in one store instruction: lane 2h + j writes word j of head h
+      // (the CU's store queue sits behind its page loads; fewer instructions wait less)
+      const int hh = lane >> 1;
+      float ml = 0.f;
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) ml = hh == h ? ((lane & 1) ? Lh[h] : Mh[h]) : ml;
+      if (lane < 2 * HPG) ll_store(p.ll_part + part_index<S>(p, l, gi, hh, s) + (lane & 1), ml, epoch);
     }
   }
   if (g.s_eff > 1 && s < HPG) {
