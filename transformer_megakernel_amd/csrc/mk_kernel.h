@@ -82,14 +82,15 @@ struct Traced : B {
   static constexpr bool TRACE = true;
 };
 
-// Attention items with several splits.  head_dim 64: on the matrix units, every compute
-// wave taking a quarter of each page's keys for all of the group's query heads (KS = 4
-// key subsets); otherwise one query head per wave (KS = MK_NC / HPG subsets per head).
+// Attention items with several splits.  On the matrix units (head_dim 64 or 128), every
+// compute wave taking 16 keys of its pages for all of the group's query heads (KS = 4 key
+// subsets); otherwise one query head per wave (KS = MK_NC / HPG subsets per head).
 // The subsets' partials (m, l, o) per head go to the activation slot, after q|k|v, where
 // there is room, else to their own LDS array.
 template <class S>
 struct AttnGeo {
-  static constexpr bool MMA = S::HD == 64 && S::HPG <= 4 && S::PPP == 64;
+  static constexpr bool MMA = (S::HD == 64 || S::HD == 128) && S::HPG <= 4 && S::PPP % 16 == 0 &&
+                              MK_NC % (S::PPP / 16) == 0;
   static constexpr int KS = MMA ? MK_NC : MK_NC / S::HPG;
   static constexpr int PART = KS * S::HPG * (S::HD + 2);     // floats of partials
   static constexpr int OFF = (S::GRP + 63) / 64 * 64;        // their offset in the slot
@@ -965,9 +966,9 @@ __device__ __forceinline__ size_t part_index(const MkParams& p, int l, int g, in
 
 // ------------------------------------------------------------------ attention
 // Short contexts (one split, q-head mode): item (g, b) is query head b of KV group g and
-// the four compute waves split the keys.  Several splits: head_dim 64 goes to the matrix
-// units (attn_run_mma: each wave a quarter of every page's keys, all heads).  Otherwise
-// compute wave w handles query head h = w % HPG of the item's KV group over the key
+// the four compute waves split the keys.  Several splits: the matrix units (attn_run_mma:
+// each wave 16 keys of its pages for all heads).  Shapes the matrix-unit form does not
+// cover keep the VALU one: compute wave w handles query head h = w % HPG of the item's KV group over the key
 // subset t = w / HPG (pages t, t + NSUB, ... of the split; NSUB = MK_NC / HPG): with four
 // query heads per KV head every wave sees every page and owns its head outright, so no
 // cross-wave merge is needed.  Each page is read by HPG waves and freed by the last.
@@ -1048,14 +1049,20 @@ __device__ __forceinline__ float* part_base(MkShared<S>& sh, const float* act) {
   else return sh.part;
 }
 
-// Attention over the item's cached keys on the matrix units (head_dim 64, several splits):
-// wave w takes keys 16w..16w+15 of every page for all of the group's query heads, so
-// each K/V element is unpacked once per CU instead of once per head.  Per page:
-//   S = K q   (16 keys x 16 head columns, two 16x16x32 bf16 products per 32 dims; q is
-//              split into bf16 hi + lo parts, so the scores keep ~16 significant bits),
+// Attention over the item's cached keys on the matrix units (several splits): a wave takes
+// 16 keys of a page for all of the group's query heads, so each K/V element is unpacked
+// once per CU instead of once per head (head_dim 64: 64 keys per page, wave w keys 16w..
+// of every page; head_dim 128: 32 keys per page, waves 0-1 the even pages and 2-3 the
+// odd ones, 16 keys each).  Per page:
+//   S = K q   (16 keys x 16 head columns, 16x16x32 bf16 products; q is split into three
+//              bf16 parts hi + mid + lo, exact to ~2^-24, so the scores keep fp32
+//              accuracy: with two parts (~16 bits), errors the score's size amplifies
+//              let the 32-layer 8B shape's appended K/V drift past the fp32 bound),
 //   an online softmax per head over the wave's keys (its running max is shared by the
 //   four lanes of a column),
-//   O += P V  (16 heads x 64 dims as four 16x16x16 bf16 products; P split hi + lo).
+//   O += P V  (16 heads x hd dims as hd/16 16x16x16 bf16 products; P in [0, 1] is split
+//              into bf16 hi + lo, ~2^-17, which keeps that bound; a third part cost
+//              ~3 us per step at context 8192).
 // Operand layouts (lane l, c = l % 16, g = l / 16): A[row c][k 8g..] (16x16x32) or
 // [row c][k 4g..] (16x16x16); B[k ...][column c]; C/D[rows 4g..4g+3][column c].  The
 // scores' C layout (key 4g + i, head c) is exactly the A layout P needs (head c, key
@@ -1065,63 +1072,72 @@ template <class S>
 __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
                                              const float* act, int base, int w, int lane, u64& waited) {
   constexpr int HD = S::HD, HPG = S::HPG, NSLOT = Ring<S>::NSLOT;
-  static_assert(AttnGeo<S>::MMA && HD == 64 && S::PPP == 64 && MK_NC == 4, "matrix-unit attention shape");
+  constexpr int KB = HD / 32, NT = HD / 16;                 // 32-dim blocks of S, 16-dim tiles of O
+  constexpr int WPP = S::PPP / 16, STR = MK_NC / WPP;       // waves per page, page stride per wave
+  static_assert(AttnGeo<S>::MMA && MK_NC == 4, "matrix-unit attention shape");
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int c = lane & 15, g = lane >> 4;
   // q as B: column c = head, k = dims 8g + 32kk + e (padding columns read head 0's q and
   // take zeros)
-  bf16x8 qh[2], ql[2];
+  bf16x8 qh[KB], qm[KB], ql[KB];
   const float* qc = act + (c < HPG ? c : 0) * HD + 8 * g;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < KB; ++kk) {
     const float4 x0 = *(const float4*)(qc + 32 * kk), x1 = *(const float4*)(qc + 32 * kk + 4);
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = c < HPG ? xs[e] : 0.f;
       const uint32_t xb = __float_as_uint(x);
+      const float r1 = x - __uint_as_float(xb & 0xffff0000u);
+      const uint32_t rb = __float_as_uint(r1);
       qh[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)(xb >> 16));
-      ql[kk][e] = __builtin_bit_cast(__bf16, f2bf_finite(x - __uint_as_float(xb & 0xffff0000u)));
+      qm[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)(rb >> 16));
+      ql[kk][e] = __builtin_bit_cast(__bf16, f2bf_finite(r1 - __uint_as_float(rb & 0xffff0000u)));
     }
   }
-  f32x4 o[4];
+  f32x4 o[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;   // running max of head c; this lane's part of its denominator
   int prev_k = -1, prev_old = 0;
   auto release_prev = [&]() {
     if (prev_k >= 0) {
       const int old = __builtin_amdgcn_readlane(prev_old, 0);   // lane 0's count, no LDS trip
-      if (old == MK_NC - 1 && lane == 0) {
+      if (old == WPP - 1 && lane == 0) {
         sh.acnt[prev_k % NSLOT] = 0;
         lds_store(&sh.freed[prev_k % NSLOT], prev_k + 1);
       }
       prev_k = -1;
     }
   };
-  const int kr = 16 * w + c;            // the key row this lane loads for A = K
-  const int vr = 16 * w + 4 * g;        // first of the four key rows it loads for B = V
-  for (int pg = 0; pg < d.np; ++pg) {
+  const int kw = 16 * (w % WPP);        // the wave's first key in each of its pages
+  const int kr = kw + c;                // the key row this lane loads for A = K
+  const int vr = kw + 4 * g;            // first of the four key rows it loads for B = V
+  for (int pg = w / WPP; pg < d.np; pg += STR) {
     const int k = base + pg;
     const char* page = page_wait<S>(p, sh, ring_base, k, waited);
     if (!page) return false;
     const int npos = min(S::PPP, d.ce - (d.j0 + pg * S::PPP));
     // keys [npos][HD], then values [npos][HD]; rows past npos hold copies of cached rows
-    const bf16x8 k0 = *(const bf16x8*)(page + kr * (HD * 2) + g * 16);
-    const bf16x8 k1 = *(const bf16x8*)(page + kr * (HD * 2) + g * 16 + 64);
-    const char* vb = page + npos * (HD * 2) + vr * (HD * 2) + c * 2;
-    i16x4 vv[4];
+    bf16x8 kb[KB];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int kk = 0; kk < KB; ++kk) kb[kk] = *(const bf16x8*)(page + kr * (HD * 2) + g * 16 + kk * 64);
+    const char* vb = page + npos * (HD * 2) + vr * (HD * 2) + c * 2;
+    i16x4 vv[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) vv[nt][j] = *(const short*)(vb + j * (HD * 2) + nt * 32);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qh[0], sc, 0, 0, 0);
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, ql[0], sc, 0, 0, 0);
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qh[1], sc, 0, 0, 0);
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, ql[1], sc, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qh[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qm[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], ql[kk], sc, 0, 0, 0);
+    }
     float sv[4], pm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1151,7 +1167,7 @@ __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh,
 #pragma unroll
     for (int i = 0; i < 4; ++i) ah[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[nt][i] *= ah[i];
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vv[nt], o[nt], 0, 0, 0);
@@ -1175,7 +1191,7 @@ __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh,
   }
   if (g == 0) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < HPG; ++i) part[i * (HD + 2) + 2 + 16 * nt + c] = o[nt][i];
   }
