@@ -809,6 +809,15 @@ __device__ __forceinline__ int qkv_index(int row) {
   return (r / S::HD) * S::GRP + (S::HPG + 1) * S::HD + (r % S::HD);
 }
 
+// The down chunk before the held ones: at its start waves 0 and 1 issue the loads of
+// their held pages of the next chunk (16 per wave, which wait behind the CU's page
+// stream), so its two ring pages go whole to waves 2 and 3 instead of being shared by the
+// four waves (2 us per step faster).
+template <class S>
+__device__ __forceinline__ bool whole_pages_23(const Dec& d) {
+  return hold_down<S>() && S::NCH >= 3 && MK_NC == 4 && d.op == MK_OP_DOWN && d.a == S::NCH - 3 && d.np == 2;
+}
+
 // One GEMV instruction on the wave's pages.  The lane's slice of the activation stays in
 // registers for the whole instruction.  Per page: every row's partial dot product, one
 // combined cross-lane reduction for all rows of the page, then the rows' epilogues run
@@ -859,7 +868,7 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
   // page is shared by two waves, one per pair of its rows, halving the time the
   // instruction spends on its critical path.
   if constexpr (MK_SPLIT_PAGES && AREG && R::WIDE && R::RPP == 4 && MK_NC == 4) {
-    if ((d.op == MK_OP_O || d.op == MK_OP_DOWN) && d.np == 2 && d.rp == 0 && mode == 0) {
+    if ((d.op == MK_OP_O || (d.op == MK_OP_DOWN && !whole_pages_23<S>(d))) && d.np == 2 && d.rp == 0 && mode == 0) {
       constexpr int NSLOT = Ring<S>::NSLOT;
       const int pgi = w >> 1, h = w & 1, k = base + pgi;
       const char* page = page_wait<S>(p, sh, ring_base, k, waited);
@@ -948,7 +957,7 @@ __device__ __forceinline__ bool gemv(const MkParams& p, MkShared<S>& sh, const c
     if (mode != 2 && w >= d.rw && w < d.rw + d.rp) page_body(hold, w - d.rw, -1);
   }
   if (mode == 1) return true;
-  for (int pg = first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
+  for (int pg = whole_pages_23<S>(d) ? (w >= 2 ? w - 2 : d.np) : first_of(w, base, MK_NC); pg < d.np; pg += MK_NC) {
     const char* page = page_wait<S>(p, sh, ring_base, base + pg, waited);
     if (!page) return false;
     uint4 wv[R::USED];
