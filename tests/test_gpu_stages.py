@@ -88,5 +88,15 @@ def test_stages_llama1b():
 
 def test_stages_small_shape_head_dim_128_split_kv():
     """head_dim 128 with the cached keys split over four CUs per KV head (256 keys each),
-    a fifth split holding only the current position, and the splits merged."""
+    the current position joining the last split, and the splits merged."""
     run_stage_check(SMALL128, 1100, 1024, 1024, 5)
+
+
+@pytest.mark.parametrize("shape,pos", [(SMALL128, 1024 + 20), (SMALL128, 1024 + 70), (SMALL, 512 + 20),
+                                       (SMALL, 512 + 150)])
+def test_stages_split_kv_partial_last_split(shape, pos):
+    """The last split with a partial page: head_dim 128 (32 keys a page, two waves a page)
+    with one page of 20 keys (the pages' second pair of waves has none) or three pages
+    (an odd count, the last of 6 keys); head_dim 64 (64 keys a page, a wave per 16 keys)
+    with 20 keys (three of the four waves see only keys past the end) or 150."""
+    run_stage_check(shape, pos + 8, pos, pos, 9)
