@@ -116,6 +116,7 @@ struct __align__(16) MkShared {
   uint32_t tr[S::TRACE ? MK_TRACE_MAX : 1][MK_TRACE_SLOTS];   // the trace: ticks after t0 (slots 9, 11: durations)
   unsigned long long t0;                    // s_memrealtime at the work-group's start
   int act_seq;                              // instructions staged by the leader
+  int pcnt;                                 // matrix-unit attention partials written (per wave)
   int abort_flag;
   uint32_t epoch;                           // tag of this step's words
   int token;                                // input token (validated)
@@ -1076,10 +1077,12 @@ __device__ __forceinline__ float* part_base(MkShared<S>& sh, const float* act) {
 // [row c][k 4g..] (16x16x16); B[k ...][column c]; C/D[rows 4g..4g+3][column c].  The
 // scores' C layout (key 4g + i, head c) is exactly the A layout P needs (head c, key
 // 4g + j), so P goes from softmax to the product without moving.  Columns c >= HPG are
-// padding (q = 0, P = 0).  The partials go to the leader, which adds the current key.
+// padding (q = 0, P = 0).  The waves' partials meet in LDS; then wave h folds head h's
+// with the current key and publishes the split's (m, l, o) for that head.
 template <class S>
 __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
-                                             const float* act, int base, int w, int lane, u64& waited) {
+                                             const StepGeo& sg, const float* act, int base, int w, int lane,
+                                             uint32_t epoch, int& nmma, u64& waited) {
   constexpr int HD = S::HD, HPG = S::HPG, NSLOT = Ring<S>::NSLOT;
   constexpr int KB = HD / 32, NT = HD / 16;                 // 32-dim blocks of S, 16-dim tiles of O
   constexpr int WPP = S::PPP / 16, STR = MK_NC / WPP;       // waves per page, page stride per wave
@@ -1204,6 +1207,55 @@ __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh,
 #pragma unroll
       for (int i = 0; i < HPG; ++i) part[i * (HD + 2) + 2 + 16 * nt + c] = o[nt][i];
   }
+  // Once every wave's partials are in, wave h folds head h's four with the current key
+  // and publishes the split's (m, l, o) of that head (the heads in parallel, not one
+  // after another on the leader).
+  lds_fence();
+  if (lane == 0) __hip_atomic_fetch_add(&sh.pcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  ++nmma;
+  if (!wait_flag(p, sh, &sh.pcnt, MK_NC * nmma, false)) return false;
+  if (w < HPG) {
+    constexpr int E = HD / 64, STRIDE = HD + 2;
+    const int h = w;
+    const float* pb = part_base<S>(sh, act);
+    float mw[MK_NC], lw[MK_NC], ow[MK_NC][E];
+#pragma unroll
+    for (int t = 0; t < MK_NC; ++t) {
+      const float* q = pb + (t * HPG + h) * STRIDE;
+      mw[t] = q[0];
+      lw[t] = q[1];
+#pragma unroll
+      for (int cc = 0; cc < E; ++cc) ow[t][cc] = q[2 + cc * 64 + lane];
+    }
+    const bool has_pos = d.b == sg.s_eff - 1;
+    float sp = -INFINITY;
+    if (has_pos) {
+      float a = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < E; ++cc) a = fmaf(act[h * HD + cc * 64 + lane], act[HPG * HD + cc * 64 + lane], a);
+      sp = wave_sum(a) * p.attn_scale;
+    }
+    float M = sp;
+#pragma unroll
+    for (int t = 0; t < MK_NC; ++t) M = fmaxf(M, mw[t]);
+    float Lt = 0.f, wt[MK_NC];
+#pragma unroll
+    for (int t = 0; t < MK_NC; ++t) {
+      wt[t] = mw[t] == -INFINITY ? 0.f : __expf(mw[t] - M);
+      Lt = fmaf(lw[t], wt[t], Lt);
+    }
+    const float wp = has_pos ? __expf(sp - M) : 0.f;
+    Lt += wp;
+    u64* dst = p.ll_part + part_index<S>(p, d.layer, d.a, h, d.b);
+#pragma unroll
+    for (int cc = 0; cc < E; ++cc) {
+      float oo = wp * act[(HPG + 1) * HD + cc * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < MK_NC; ++t) oo = fmaf(ow[t][cc], wt[t], oo);
+      ll_store(dst + 2 + cc * 64 + lane, oo, epoch);
+    }
+    if (lane < 2) ll_store(dst + lane, lane ? Lt : M, epoch);
+  }
   return true;
 }
 
@@ -1214,10 +1266,10 @@ __device__ __forceinline__ bool attn_run_mma(const MkParams& p, MkShared<S>& sh,
 template <class S>
 __device__ __forceinline__ bool attn_run(const MkParams& p, MkShared<S>& sh, const char* ring_base, const Dec& d,
                                          const StepGeo& g, const float* act, int base, int w, int lane,
-                                         uint32_t epoch, u64& waited) {
+                                         uint32_t epoch, int& nmma, u64& waited) {
   constexpr int HD = S::HD, HPG = S::HPG, LPP = HD / 8, NSUB = MK_NC / HPG, NSLOT = Ring<S>::NSLOT;
   if constexpr (AttnGeo<S>::MMA) {
-    if (!g.qh) return attn_run_mma<S>(p, sh, ring_base, d, act, base, w, lane, waited);
+    if (!g.qh) return attn_run_mma<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch, nmma, waited);
   }
   // q-head mode: head d.b of the group; every wave reads every page and takes units
   // w, w + MK_NC of it.  Otherwise one head per wave (w % HPG) over pages t, t + NSUB, ...
@@ -1360,6 +1412,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
                                              int nins, const StepGeo& g, int w, int lane, uint32_t epoch) {
   int base = 0;   // ring number of the instruction's first page
   u64 best = 0;
+  int nmma = 0;   // matrix-unit attention items done (their partial count in LDS)
   // Held pages.  Each compute wave keeps one weight page in registers (64 VGPRs), loaded
   // ahead of its instruction with plain non-temporal loads; the loaders skip those pages,
   // so the LDS ring reaches that much further ahead.  Per layer a wave holds its gate/up
@@ -1420,7 +1473,7 @@ __device__ __forceinline__ void compute_wave(const MkParams& p, MkShared<S>& sh,
     bool ok = true;
     u64 waited = 0;
     if (d.op == MK_OP_ATTN) {
-      if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch, waited);
+      if (attn_active(g, d.b, S::HPG)) ok = attn_run<S>(p, sh, ring_base, d, g, act, base, w, lane, epoch, nmma, waited);
     } else if constexpr (S::NQ == S::D && S::KC == S::D) {
       // every matrix-vector instruction has rows of the same length: one copy of the code
       // (the instruction cache holds the kernel's hot code better that way)
@@ -1648,10 +1701,10 @@ __device__ __forceinline__ bool stage_attn(const MkParams& p, MkShared<S>& sh, c
   return true;
 }
 
-// After the compute waves.  With fewer query heads per KV head than compute waves, the
-// waves of one head covered disjoint key subsets: combine their partials (and the
-// current position's key) into this split's (m, l, o), then write o (single split) or
-// publish the split.  Then, with several splits, CUs whose split index is below the
+// After the compute waves.  With fewer query heads per KV head than compute waves (and
+// not the matrix-unit form, whose waves do this themselves), the waves of one head covered
+// disjoint key subsets: combine their partials (and the current position's key) into this
+// split's (m, l, o), then write o (single split) or publish the split.  Then, with several splits, CUs whose split index is below the
 // heads per group merge one head each over all splits.  Lane `lane` handles elements
 // lane + 64c of each head.
 template <class S>
@@ -1703,7 +1756,7 @@ __device__ __forceinline__ bool attn_finalize(const MkParams& p, MkShared<S>& sh
     }
     return true;
   }
-  if (NSUB > 1 && s < g.s_eff) {
+  if (NSUB > 1 && !AttnGeo<S>::MMA && s < g.s_eff) {
     const bool has_pos = s == g.s_eff - 1;
     const float* pb = part_base<S>(sh, act);
     float mw[NSUB][HPG], lw[NSUB][HPG], ow[NSUB][HPG][E], qv[HPG][E], kn[E], vn[E];
@@ -1903,10 +1956,11 @@ __device__ __forceinline__ void leader_wave(const MkParams& p, MkShared<S>& sh, 
     if (lane == 0) lds_store(&sh.act_seq, i + 1);
     trace_mark<S>(p, sh, i, 4, lane);
     if (in.op == MK_OP_ATTN) {
-      // Partials in LDS only when several waves share a head; a merge polls global words.
-      // (In q-head mode attn_finalize waits itself, after the current key's score.)
+      // Partials in LDS only when several waves share a head (the matrix-unit form folds
+      // them in the compute waves themselves); a merge polls global words.  (In q-head
+      // mode attn_finalize waits itself, after the current key's score.)
       if (!g.qh) {
-        if (AttnGeo<S>::KS > 1 && !wait_all_done(p, sh, i + 1, true)) return;
+        if (AttnGeo<S>::KS > 1 && !AttnGeo<S>::MMA && !wait_all_done(p, sh, i + 1, true)) return;
         trace_mark<S>(p, sh, i, 8, lane);
       }
       if (!attn_finalize<S>(p, sh, in, g, i, epoch, lane)) return;
@@ -1945,6 +1999,7 @@ __global__ void __launch_bounds__(MK_THREADS) mk_step_kernel(MkParams p) {
   if (threadIdx.x == 0) {
     sh.t0 = __builtin_amdgcn_s_memrealtime();
     sh.act_seq = 0;
+    sh.pcnt = 0;
     // A step launched after an earlier one was abandoned (device error not yet reported
     // and reset by the host) does nothing: the communication words and the ticket may
     // still hold that step's partial state, and its words carry the current epoch.
