@@ -26,7 +26,8 @@ QKV, ATTN, O, GATEUP, DOWN, LMHEAD = 1, 2, 3, 4, 5, 6
 def split_geometry(shape, plan, pos):
     ppp = plan["page_bytes"] // (4 * shape.head_dim)
     nk = max(pos, 1)   # the cached keys 0..pos-1 (the current key joins the last split)
-    chunk = max(256, math.ceil(nk / plan["s_max"]))
+    min_chunk = 128 if shape.head_dim == 64 else 256   # the host plan's fewest keys per split
+    chunk = max(min_chunk, math.ceil(nk / plan["s_max"]))
     chunk = math.ceil(chunk / ppp) * ppp
     return math.ceil(nk / chunk)
 

@@ -181,14 +181,16 @@ def test_plan_simulator_reports_planted_deadlocks(pos):
     assert not simulate(s, circular, pos)[0]
 
 
-@pytest.mark.parametrize("pos,splits", [(0, 1), (1, 1), (128, 1), (256, 1), (257, 2), (300, 2),
-                                        (1024, 4), (1279, 5), (8191, 32), (8192, 32)])
-def test_attention_splits_cover_the_cached_keys(pos, splits):
-    """Keys 0..pos-1 are in the cache and split into runs of at least 256 (a whole number
-    of pages), at most one per CU of a KV head's share; the current key joins the last
-    split, so no split ever holds it alone."""
+@pytest.mark.parametrize("name,pos,splits", [
+    ("llama1b", 0, 1), ("llama1b", 1, 1), ("llama1b", 128, 1), ("llama1b", 129, 2), ("llama1b", 256, 2),
+    ("llama1b", 300, 3), ("llama1b", 1024, 8), ("llama1b", 1279, 10), ("llama1b", 8191, 32),
+    ("llama1b", 8192, 32), ("llama8b", 256, 1), ("llama8b", 257, 2), ("llama8b", 2048, 8)])
+def test_attention_splits_cover_the_cached_keys(name, pos, splits):
+    """Keys 0..pos-1 are in the cache and split into runs of at least 128 keys at head_dim
+    64 (256 at head_dim 128), a whole number of pages, at most one per CU of a KV head's
+    share; the current key joins the last split, so no split ever holds it alone."""
     from tests.plan_sim import split_geometry
-    s = ModelShape.named("llama1b")
+    s = ModelShape.named(name)
     P = mk.Megakernel.plan_only(s, 8193, 256).plan()
     assert P["s_max"] == 32
     assert split_geometry(s, P, pos) == splits

@@ -125,8 +125,8 @@ def test_tiny_device_token_chain():
     greedy_compare(M, synth.make_token(M.shape, 2), 16, 8, dev_chain=True)
 
 
-def test_tiny_two_splits_merge_path():
-    """pos 300: keys split in two, merged across CUs."""
+def test_tiny_split_kv_merge_path():
+    """pos 300: the 300 cached keys in three splits (128, 128, 44), merged across CUs."""
     M = Model("tiny", 512, 300)
     greedy_compare(M, 77, 300, 3)
 
@@ -246,8 +246,9 @@ def test_llama1b_context_128_one_step(w1b):
     greedy_compare(M, synth.make_token(shape, 2), 128, 1)
 
 
-def test_llama1b_context_700_three_splits(w1b):
-    """701 keys: three splits of 256 keys per KV head, merged across CUs."""
+def test_llama1b_context_700_split_kv(w1b):
+    """Context 700: six splits per KV head (five of 128 cached keys, one of 60 with the
+    current key), merged across CUs."""
     shape, W = w1b
     M = Model("llama1b", 704, 700, shape=shape, W=W)
     greedy_compare(M, 4321, 700, 2)

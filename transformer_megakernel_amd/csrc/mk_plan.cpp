@@ -101,7 +101,12 @@ int mk_build_plan(const mk_config& c, int n_cus, MkPlan* out, std::string* why) 
   p.page_bytes = MK_PAGE_BYTES;
   // The merge of one head's splits polls 16 splits per round; 32 keeps it to two rounds.
   p.s_max = std::max(1, std::min(n_cus / c.n_kv_heads, 32));
-  p.min_chunk = 256;
+  // Fewest cached keys per split.  At head_dim 64 (the matrix-unit attention takes a wave
+  // ~0.45 us per 64-key page) two pages: more CUs per KV head at medium contexts (256
+  // greedy steps from context 1024: 595 -> 580 us per step).  At head_dim 128 four
+  // 32-key pages: 128-key splits there pushed one of the 8B step's appended K/V elements
+  // past the fp32 bound of the parity test.
+  p.min_chunk = c.head_dim == 64 ? 128 : 256;
   if (p.s_max < c.n_q_heads / c.n_kv_heads) {
     if (why) *why = "too few CUs for one merger per query head of a group";
     return MK_EINVAL;
