@@ -93,10 +93,11 @@ def test_stages_small_shape_head_dim_128_split_kv():
 
 
 @pytest.mark.parametrize("shape,pos", [(SMALL128, 1024 + 20), (SMALL128, 1024 + 70), (SMALL, 512 + 20),
-                                       (SMALL, 512 + 150)])
+                                       (SMALL, 512 + 100)])
 def test_stages_split_kv_partial_last_split(shape, pos):
-    """The last split with a partial page: head_dim 128 (32 keys a page, two waves a page)
-    with one page of 20 keys (the pages' second pair of waves has none) or three pages
-    (an odd count, the last of 6 keys); head_dim 64 (64 keys a page, a wave per 16 keys)
-    with 20 keys (three of the four waves see only keys past the end) or 150."""
+    """The last split with a partial page: head_dim 128 (256-key splits of 32-key pages,
+    two waves a page) with one page of 20 keys (the pages' second pair of waves has none)
+    or three pages (an odd count, the last of 6 keys); head_dim 64 (128-key splits of
+    64-key pages, a wave per 16 keys) with 20 keys (three of the four waves see only keys
+    past the end) or 100 (two pages, the second of 36 keys)."""
     run_stage_check(shape, pos + 8, pos, pos, 9)
